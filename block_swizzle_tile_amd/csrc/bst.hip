@@ -1,0 +1,515 @@
+// bst.hip -- host side of the C ABI declared in include/bst.h: argument
+// validation (pure host code, no HIP call before it passes), kernel-instance
+// selection, schedule resolution (default tiles, automatic K split,
+// persistent grid size) and launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "bst.h"
+#include "bst_device.hpp"
+
+using namespace bst;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bst_status fail(bst_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+// ------------------------------------------------------------ instances ---
+using LaunchFn = hipError_t (*)(dim3, dim3, hipStream_t, const GemmArgs&);
+
+struct Instance {
+  int ab;  // AbKind (AB_MXE4M3 shares the AB_E4M3 kernels)
+  int bm, bn;
+  bool grouped;
+  const void* fn;
+  LaunchFn launch;
+  int threads;
+  int bk;
+};
+
+template <int AB, int BM, int BN, int WM, int WN, bool GR>
+hipError_t launch_impl(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
+  hipLaunchKernelGGL((gemm_kernel<AB, BM, BN, WM, WN, GR>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+#define BST_INST(AB, BM, BN, WM, WN, GR)                                                  \
+  Instance {                                                                              \
+    AB, BM, BN, GR, reinterpret_cast<const void*>(&gemm_kernel<AB, BM, BN, WM, WN, GR>), \
+        &launch_impl<AB, BM, BN, WM, WN, GR>, 64 * WM * WN, Traits<AB>::BK                \
+  }
+
+const Instance kInstances[] = {
+    BST_INST(AB_F16, 64, 64, 2, 2, false),
+    BST_INST(AB_F16, 128, 128, 2, 2, false),
+    BST_INST(AB_F16, 256, 128, 2, 2, false),
+    BST_INST(AB_F16, 128, 256, 2, 2, false),
+    BST_INST(AB_F16, 128, 192, 2, 2, false),
+    BST_INST(AB_F16, 128, 128, 2, 2, true),
+    BST_INST(AB_BF16, 64, 64, 2, 2, false),
+    BST_INST(AB_BF16, 128, 128, 2, 2, false),
+    BST_INST(AB_BF16, 256, 128, 2, 2, false),
+    BST_INST(AB_BF16, 128, 256, 2, 2, false),
+    BST_INST(AB_BF16, 128, 192, 2, 2, false),
+    BST_INST(AB_BF16, 128, 128, 2, 2, true),
+    BST_INST(AB_I8, 64, 64, 2, 2, false),
+    BST_INST(AB_I8, 128, 128, 2, 2, false),
+    BST_INST(AB_I8, 256, 128, 2, 2, false),
+    BST_INST(AB_I8, 256, 256, 2, 2, false),
+    BST_INST(AB_I8, 64, 64, 2, 2, true),
+    BST_INST(AB_I8, 128, 128, 2, 2, true),
+    BST_INST(AB_I8, 256, 128, 2, 2, true),
+    BST_INST(AB_I8, 256, 256, 2, 2, true),
+    BST_INST(AB_E4M3, 64, 64, 2, 2, false),
+    BST_INST(AB_E4M3, 128, 128, 2, 2, false),
+    BST_INST(AB_E4M3, 256, 128, 2, 2, false),
+    BST_INST(AB_E4M3, 256, 256, 2, 2, false),
+};
+
+int kernel_ab(bst_dtype ab) { return ab == BST_MXE4M3 ? AB_E4M3 : (int)ab; }
+
+const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped) {
+  for (const Instance& in : kInstances)
+    if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
+        in.grouped == grouped)
+      return &in;
+  return nullptr;
+}
+
+size_t elem_size(bst_dtype t) {
+  switch (t) {
+    case BST_F16:
+    case BST_BF16: return 2;
+    case BST_E4M3:
+    case BST_MXE4M3:
+    case BST_I8: return 1;
+    case BST_I32:
+    case BST_F32: return 4;
+  }
+  return 0;
+}
+
+bool is_ab(bst_dtype t) {
+  return t == BST_F16 || t == BST_BF16 || t == BST_E4M3 || t == BST_MXE4M3 || t == BST_I8;
+}
+
+bool out_ok(bst_dtype ab, bst_dtype c) {
+  if (c == BST_F16 || c == BST_BF16 || c == BST_F32) return true;
+  return c == BST_I32 && ab == BST_I8;
+}
+
+// --------------------------------------------------------- device info ----
+struct DevInfo {
+  int cus = 0;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, DevInfo> g_dev;
+std::unordered_map<uint64_t, int> g_occ;
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it != g_dev.end()) return it->second.cus;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  g_dev[dev].cus = cus;
+  return cus;
+}
+
+int occupancy(const Instance* in) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  const uint64_t key = ((uint64_t)(uintptr_t)in) ^ ((uint64_t)dev << 56);
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, in->fn, in->threads, 0) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  (void)hipGetLastError();
+  g_occ[key] = n;
+  return n;
+}
+
+// ------------------------------------------------------------ planning ----
+constexpr int64_t kMaxU32 = 0x7fffffffLL;
+// Workspace layout: a fixed counter area (one arrival counter per tile) that
+// partial tiles never overwrite, then the fp32 / int32 partial tiles.  The
+// counter area must be zero before the first call; every call leaves the
+// counters it used at zero, whatever its tile count or split.
+constexpr uint32_t kMaxSplitTiles = 16384;
+constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
+
+struct Plan {
+  const Instance* inst = nullptr;
+  uint32_t bm = 0, bn = 0, bk = 0;
+  uint32_t off = 1, dir = 0, remap = 0;
+  uint32_t split = 1, kslice = 0;
+  uint64_t tile_cap = 0;  // tiles (upper bound for grouped)
+  uint32_t grid = 0;
+  size_t ws_bytes = 0;
+  size_t part_bytes = 0;
+};
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Resolves the schedule.  kind 0: plain / batched (count = batch), kind 1:
+// grouped (count = G, M = total_m).  Validates the schedule fields and the
+// sizes that bound the task count; pointer checks are the callers'.
+bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
+                     const bst_sched* s, bool need_device, Plan& p) {
+  if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
+  if (count < 0 || M < 0 || N < 0 || K < 0)
+    return fail(BST_E_INVAL, "negative size (count %lld M %lld N %lld K %lld)", (long long)count,
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxU32 || N > kMaxU32 || K > kMaxU32 || count > kMaxU32)
+    return fail(BST_E_INVAL, "size above 2^31-1");
+  if (kind == 1 && (count < 1 || count > kMaxGroups))
+    return fail(BST_E_INVAL, "group count %lld outside [1, %d]", (long long)count, kMaxGroups);
+  if (ab == BST_MXE4M3 && K % 32 != 0)
+    return fail(BST_E_INVAL, "MX operands need K %% 32 == 0 (K = %lld)", (long long)K);
+  if (ab == BST_I8 && K > 131071)
+    return fail(BST_E_INVAL, "int8 K = %lld could overflow the int32 accumulator (max 131071)",
+                (long long)K);
+  bst_sched d{};
+  if (s) d = *s;
+  if (d.swizzle_offset == 0 && s) return fail(BST_E_INVAL, "swizzle_offset must be >= 1");
+  if (!s) d.swizzle_offset = 1;
+  if (d.swizzle_direction > 2)
+    return fail(BST_E_INVAL, "swizzle_direction %u not in {0 Zn, 1 Nz, 2 raster}",
+                d.swizzle_direction);
+  if (d.xcd_remap > 1) return fail(BST_E_INVAL, "xcd_remap must be 0 or 1");
+  if (d.split_k > 64) return fail(BST_E_INVAL, "split_k %u above 64", d.split_k);
+  if (d.tile_m == 0 && d.tile_n == 0) {
+    d.tile_m = 128;
+    d.tile_n = 128;
+  }
+  p.inst = find_instance(ab, d.tile_m, d.tile_n, kind == 1);
+  if (!p.inst)
+    return fail(BST_E_UNSUPPORTED, "no %s kernel for dtype %d with tile %ux%u",
+                kind == 1 ? "grouped" : "plain", (int)ab, d.tile_m, d.tile_n);
+  if (d.tile_k != 0 && d.tile_k != (uint32_t)p.inst->bk)
+    return fail(BST_E_UNSUPPORTED, "tile_k %u: this dtype runs tile_k %d", d.tile_k,
+                p.inst->bk);
+  p.bm = d.tile_m;
+  p.bn = d.tile_n;
+  p.bk = (uint32_t)p.inst->bk;
+  p.off = d.swizzle_offset;
+  p.dir = d.swizzle_direction;
+  p.remap = d.xcd_remap;
+  const int64_t loopsN = cdiv64(N, p.bn);
+  const int64_t tiles = kind == 1 ? (cdiv64(M, p.bm) + count) * loopsN
+                                  : count * cdiv64(M, p.bm) * loopsN;
+  if (tiles > kMaxU32) return fail(BST_E_INVAL, "task count %lld above 2^31-1", (long long)tiles);
+  p.tile_cap = (uint64_t)tiles;
+  const int64_t nk = cdiv64(K, p.bk);
+  int64_t split = d.split_k;
+  const int cus = need_device ? device_cus() : 256;
+  if (split == 0) {
+    split = 1;
+    if (tiles > 0 && tiles < cus && nk >= 8)
+      split = std::min<int64_t>({cus / tiles, nk / 4, 16});
+    if (split < 1) split = 1;
+  }
+  if (nk == 0) split = 1;
+  int64_t kslice_steps = nk > 0 ? cdiv64(nk, split) : 0;
+  if (kslice_steps > 0) split = cdiv64(nk, kslice_steps);  // no empty slices
+  p.split = (uint32_t)split;
+  p.kslice = (uint32_t)(kslice_steps * p.bk);
+  if (tiles * split > kMaxU32) return fail(BST_E_INVAL, "work-unit count above 2^31-1");
+  if (p.split > 1) {
+    if (tiles > (int64_t)kMaxSplitTiles)
+      return fail(BST_E_INVAL, "split_k > 1 takes at most %u tiles (got %lld)", kMaxSplitTiles,
+                  (long long)tiles);
+    p.part_bytes = (size_t)p.split * (size_t)tiles * p.bm * p.bn * 4;
+    p.ws_bytes = kCounterBytes + p.part_bytes;
+  }
+  const int64_t units = tiles * split;
+  int64_t grid = d.grid;
+  if (grid == 0) grid = (int64_t)cus * (need_device ? occupancy(p.inst) : 1);
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, units > 0 ? units : 1));
+  p.grid = (uint32_t)grid;
+  return BST_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+bool stride_ok(int64_t ld, size_t es) { return ((uint64_t)ld * es) % 16 == 0; }
+
+bst_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (p.ws_bytes == 0) return BST_OK;
+  if (!ws || ws_bytes < p.ws_bytes)
+    return fail(BST_E_WORKSPACE, "split %u needs %zu workspace bytes (got %zu)", p.split,
+                p.ws_bytes, ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BST_E_ALIGN, "workspace not 16-byte aligned");
+  return BST_OK;
+}
+
+void fill_ws(GemmArgs& a, const Plan& p, void* ws) {
+  a.split = p.split;
+  a.kslice = p.kslice;
+  a.tile_cap = (uint32_t)p.tile_cap;
+  a.ws_part = nullptr;
+  a.ws_count = nullptr;
+  if (p.split > 1) {
+    a.ws_count = reinterpret_cast<uint32_t*>(ws);
+    a.ws_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
+  }
+}
+
+bst_status launch(const Plan& p, const GemmArgs& a, void* stream) {
+  const hipError_t e =
+      p.inst->launch(dim3(p.grid), dim3(p.inst->threads), (hipStream_t)stream, a);
+  if (e != hipSuccess) return fail(BST_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return BST_OK;
+}
+
+// Shared by gemm and batched_gemm.
+bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                 int64_t strideB, void* C, int64_t ldc, int64_t strideC, const uint8_t* sa,
+                 const uint8_t* sb, const float* rs, const float* cs, const bst_sched* s,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
+  if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
+  Plan p;
+  bst_status st = make_plan(0, ab, batch, M, N, K, s, false, p);
+  if (st != BST_OK) return st;
+  if (batch == 0 || M == 0 || N == 0) return BST_OK;
+  const size_t es = elem_size(ab), ec = elem_size(c);
+  if (!C) return fail(BST_E_INVAL, "C is NULL");
+  const bool has_k = K > 0;  // with K == 0, A and B are never read
+  if (has_k && (!A || !B)) return fail(BST_E_INVAL, "A or B is NULL");
+  if ((has_k && (lda < K || ldb < N)) || ldc < N)
+    return fail(BST_E_INVAL, "leading dimension too small (lda %lld K %lld, ldb %lld N %lld, ldc %lld)",
+                (long long)lda, (long long)K, (long long)ldb, (long long)N, (long long)ldc);
+  if (batch > 1 && (strideA < 0 || strideB < 0 || strideC < 0))
+    return fail(BST_E_INVAL, "negative batch stride");
+  if (ab == BST_MXE4M3 && has_k && (!sa || !sb)) return fail(BST_E_INVAL, "MX scales are NULL");
+  if ((rs == nullptr) != (cs == nullptr)) return fail(BST_E_INVAL, "give both dequant scales or neither");
+  if (!aligned16(C) || !stride_ok(ldc, ec) || (batch > 1 && !stride_ok(strideC, ec)) ||
+      (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
+                 (batch > 1 && (!stride_ok(strideA, es) || !stride_ok(strideB, es))))))
+    return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
+  st = make_plan(0, ab, batch, M, N, K, s, true, p);
+  if (st != BST_OK) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != BST_OK) return st;
+
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint8_t*>(C);
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+  a.strideA = batch > 1 ? strideA : 0;
+  a.strideB = batch > 1 ? strideB : 0;
+  a.strideC = batch > 1 ? strideC : 0;
+  a.sa = ab == BST_MXE4M3 ? sa : nullptr;
+  a.sb = ab == BST_MXE4M3 ? sb : nullptr;
+  a.ldsa = K / 32;
+  a.ldsb = N;
+  a.row_scale = rs;
+  a.col_scale = cs;
+  a.M = (uint32_t)M; a.N = (uint32_t)N; a.K = (uint32_t)K;
+  a.batch = (uint32_t)batch;
+  a.tiles = (uint32_t)p.tile_cap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.cdtype = (uint32_t)c;
+  fill_ws(a, p, ws);
+  return launch(p, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bst_last_error(void) { return g_err; }
+
+const char* bst_version(void) { return "bst 0.1 (gfx950)"; }
+
+bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K, const void* A,
+                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                    const uint8_t* scale_a, const uint8_t* scale_b, const bst_sched* s, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (ab != BST_MXE4M3 && (scale_a || scale_b))
+    return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
+  return dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
+               nullptr, s, ws, ws_bytes, stream);
+}
+
+bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
+                            int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B,
+                            int64_t ldb, int64_t strideB, void* C, int64_t ldc, int64_t strideC,
+                            const bst_sched* s, void* ws, size_t ws_bytes, void* stream) {
+  if (ab == BST_MXE4M3) return fail(BST_E_UNSUPPORTED, "batched MX GEMM is not provided");
+  return dense(ab, c, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, nullptr,
+               nullptr, nullptr, nullptr, s, ws, ws_bytes, stream);
+}
+
+bst_status bst_quant_gemm_per_token(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                                    const int8_t* B, int64_t ldb, const float* row_scale,
+                                    const float* col_scale, void* C, int64_t ldc, bst_dtype c,
+                                    const bst_sched* s, void* ws, size_t ws_bytes, void* stream) {
+  if (c != BST_I32 && (!row_scale || !col_scale))
+    return fail(BST_E_INVAL, "row_scale and col_scale are required for a dequantised output");
+  const bool raw = c == BST_I32;
+  return dense(BST_I8, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr,
+               raw ? nullptr : row_scale, raw ? nullptr : col_scale, s, ws, ws_bytes, stream);
+}
+
+bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const int32_t* group_m,
+                                    int64_t total_m, int64_t N, int64_t K, const void* A,
+                                    int64_t lda, const void* B, int64_t ldb, int64_t strideB,
+                                    void* C, int64_t ldc, const float* row_scale,
+                                    const float* col_scale, const bst_sched* s, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (ab != BST_I8 && ab != BST_F16 && ab != BST_BF16)
+    return fail(BST_E_UNSUPPORTED, "grouped GEMM takes int8, f16 or bf16 operands");
+  if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
+  if ((row_scale == nullptr) != (col_scale == nullptr))
+    return fail(BST_E_INVAL, "give both dequant scales or neither");
+  if (row_scale && (ab != BST_I8 || c == BST_I32))
+    return fail(BST_E_INVAL, "dequant scales need int8 operands and a floating output");
+  Plan p;
+  bst_status st = make_plan(1, ab, G, total_m, N, K, s, false, p);
+  if (st != BST_OK) return st;
+  if (!group_m) return fail(BST_E_INVAL, "group_m is NULL");
+  if (total_m == 0 || N == 0) return BST_OK;
+  const size_t es = elem_size(ab), ec = elem_size(c);
+  const bool has_k = K > 0;  // with K == 0, A and B are never read
+  if (!C || (has_k && (!A || !B))) return fail(BST_E_INVAL, "A, B or C is NULL");
+  if ((has_k && (lda < K || ldb < N || strideB < (int64_t)K * ldb)) || ldc < N)
+    return fail(BST_E_INVAL, "leading dimension or group stride too small");
+  if (!aligned16(C) || !stride_ok(ldc, ec) ||
+      (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
+                 !stride_ok(strideB, es))))
+    return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
+  st = make_plan(1, ab, G, total_m, N, K, s, true, p);
+  if (st != BST_OK) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != BST_OK) return st;
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint8_t*>(C);
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+  a.strideB = strideB;
+  a.row_scale = row_scale;
+  a.col_scale = col_scale;
+  a.group_m = group_m;
+  a.G = G;
+  a.total_m = total_m;
+  a.N = (uint32_t)N; a.K = (uint32_t)K;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.cdtype = (uint32_t)c;
+  fill_ws(a, p, ws);
+  return launch(p, a, stream);
+}
+
+bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const bst_sched* s,
+                        uint32_t* out, int64_t max_tasks, void* stream) {
+  Plan p;
+  bst_sched d{};
+  if (s) d = *s;
+  d.split_k = 1;
+  bst_status st = make_plan(0, ab, batch, M, N, 0, s ? &d : nullptr, false, p);
+  if (st != BST_OK) return st;
+  if (p.tile_cap == 0) return BST_OK;
+  if (!out) return fail(BST_E_INVAL, "out is NULL");
+  if ((int64_t)p.tile_cap > max_tasks)
+    return fail(BST_E_INVAL, "%llu tasks do not fit max_tasks %lld",
+                (unsigned long long)p.tile_cap, (long long)max_tasks);
+  GemmArgs a{};
+  a.M = (uint32_t)M; a.N = (uint32_t)N;
+  a.batch = (uint32_t)batch;
+  a.tiles = (uint32_t)p.tile_cap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.map_out = out;
+  uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, a.tiles)
+                               : (uint32_t)std::min<int64_t>(device_cus(), a.tiles);
+  hipLaunchKernelGGL((tile_map_kernel<false>), dim3(grid), dim3(64), 0, (hipStream_t)stream, a,
+                     p.bm, p.bn);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BST_E_HIP, "map kernel launch failed: %s", hipGetErrorString(e));
+  return BST_OK;
+}
+
+bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m, int64_t total_m,
+                                int64_t N, const bst_sched* s, uint32_t* out, int64_t max_tasks,
+                                void* stream) {
+  Plan p;
+  bst_sched d{};
+  if (s) d = *s;
+  d.split_k = 1;
+  bst_status st = make_plan(1, ab, G, total_m, N, 0, s ? &d : nullptr, false, p);
+  if (st != BST_OK) return st;
+  if (!group_m || !out) return fail(BST_E_INVAL, "group_m or out is NULL");
+  if ((int64_t)p.tile_cap > max_tasks)
+    return fail(BST_E_INVAL, "max_tasks %lld below the bound %llu", (long long)max_tasks,
+                (unsigned long long)p.tile_cap);
+  if (p.tile_cap == 0) return BST_OK;
+  GemmArgs a{};
+  a.N = (uint32_t)N;
+  a.group_m = group_m;
+  a.G = G;
+  a.total_m = total_m;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.map_out = out;
+  uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, (uint32_t)p.tile_cap)
+                               : (uint32_t)std::min<int64_t>(device_cus(), p.tile_cap);
+  hipLaunchKernelGGL((tile_map_kernel<true>), dim3(grid), dim3(64), 0, (hipStream_t)stream, a,
+                     p.bm, p.bn);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BST_E_HIP, "map kernel launch failed: %s", hipGetErrorString(e));
+  return BST_OK;
+}
+
+size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
+                           const bst_sched* s) {
+  Plan p;
+  if (kind != 0 && kind != 1) {
+    fail(BST_E_INVAL, "kind must be 0 or 1");
+    return 0;
+  }
+  if (make_plan(kind, ab, count, M, N, K, s, true, p) != BST_OK) return 0;
+  return p.ws_bytes;
+}
+
+bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
+                               int64_t K, const bst_sched* s, bst_sched* out) {
+  if (!out) return fail(BST_E_INVAL, "out is NULL");
+  if (kind != 0 && kind != 1) return fail(BST_E_INVAL, "kind must be 0 or 1");
+  Plan p;
+  const bst_status st = make_plan(kind, ab, count, M, N, K, s, true, p);
+  if (st != BST_OK) return st;
+  out->tile_m = p.bm;
+  out->tile_n = p.bn;
+  out->tile_k = p.bk;
+  out->swizzle_offset = p.off;
+  out->swizzle_direction = p.dir;
+  out->split_k = p.split;
+  out->xcd_remap = p.remap;
+  out->grid = p.grid;
+  return BST_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,718 @@
+// bst_device.hpp -- device side of the swizzled tiled GEMM for gfx950.
+//
+// One persistent kernel template serves every form (plain, batched, grouped
+// slice-M, int8 with dequant) and every operand type:
+//   * the block -> tile scheduler of GemmIdentityBlockSwizzle ("Block
+//     Scheduler Code Explained", CATLASS docs: s4.1 loop counts, s4.4 batch
+//     index, s4.5 Zn / Nz windows with snake reversal, s4.6 tail shapes, s6
+//     runtime offset / direction) evaluated per task in scalar registers;
+//   * an optional K split (unit u -> slice u / T, task u % T, in the manner
+//     of GetBatchIdx) with an in-kernel, fixed-order fix-up;
+//   * a double-buffered global -> LDS pipeline: 16-byte coalesced loads,
+//     LDS rows of 128 bytes (one K stage) whose 16-byte chunks are
+//     XOR-permuted by the row index so that MFMA fragment reads and stage
+//     writes spread over all banks; B (row-major K x N) is transposed in
+//     registers on its way into LDS so that every MFMA operand is K-packed;
+//   * the 32x32 MFMA family of CDNA4 (f16 / bf16 x16, i8 x32, scaled fp8
+//     x64) with operands swapped (B^T as src0, A^T as src1) so that each lane
+//     ends up holding four consecutive output columns of one row;
+//   * tail masking on every load and store, and an epilogue that converts to
+//     f16 / bf16 / f32 / i32 and optionally applies the per-token x
+//     per-channel dequant in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace bst {
+
+enum AbKind { AB_F16 = 1, AB_BF16 = 2, AB_E4M3 = 3, AB_MXE4M3 = 4, AB_I8 = 5 };
+enum OutKind { OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 6, OUT_F32 = 7 };
+
+constexpr int kRowBytes = 128;      // bytes of one LDS row = one K stage of one row
+constexpr int kMaxGroups = 1024;
+constexpr int kNumXcd = 8;          // MI355X: 8 accelerator dies, one L2 each
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ arguments ---
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  uint8_t* C;
+  int64_t lda, ldb, ldc;              // elements
+  int64_t strideA, strideB, strideC;  // elements; batch (or group, for B) strides
+  const uint8_t* sa;                  // MX scales of A [M][ldsa]
+  const uint8_t* sb;                  // MX scales of B [K/32][ldsb]
+  int64_t ldsa, ldsb;
+  const float* row_scale;             // dequant, per stacked row
+  const float* col_scale;             // dequant, [G][N]
+  const int32_t* group_m;             // grouped: device int32[G]
+  int32_t G;
+  int64_t total_m;                    // grouped: rows allocated in A and C
+  uint32_t M, N, K;                   // M unused when grouped
+  uint32_t batch;
+  uint32_t tiles;                     // non-grouped: batch * loopsM * loopsN
+  uint32_t off, dir;
+  uint32_t split;                     // K slices per tile (>= 1)
+  uint32_t kslice;                    // K elements per slice (multiple of the stage depth)
+  uint32_t remap;                     // XCD-contiguous renumbering of workgroups
+  uint32_t cdtype;                    // OutKind
+  float* ws_part;                     // split > 1: [split][tile capacity][BM*BN] partials
+  uint32_t* ws_count;                 // split > 1: one arrival counter per tile
+  uint32_t tile_cap;                  // tiles the workspace was sized for
+  uint32_t* map_out;                  // map-dump kernel only
+};
+
+// ------------------------------------------------------------ scheduler ---
+// Block coordinate of the `inner`-th task of one loopsM x loopsN problem
+// (s4.5 GetBlockCoord).  An offset beyond the tile count gives the same
+// order as one window, so it is clamped first; that keeps every product in
+// 32 bits.
+struct TileCoord {
+  uint32_t m, n;
+};
+
+__device__ __forceinline__ TileCoord block_coord(uint32_t loopsM, uint32_t loopsN, uint32_t off,
+                                                 uint32_t dir, uint32_t inner) {
+  TileCoord c;
+  if (dir == 0) {  // Zn
+    const uint32_t o = off < loopsM ? off : loopsM;
+    const uint32_t span = o * loopsN;
+    const uint32_t w = inner / span;
+    const uint32_t j = inner - w * span;
+    const uint32_t windows = (loopsM + o - 1) / o;
+    const uint32_t rows = (w == windows - 1) ? loopsM - o * w : o;
+    c.m = w * o + j % rows;
+    c.n = j / rows;
+    if (w & 1u) c.n = loopsN - 1 - c.n;  // snake (s5.2)
+  } else if (dir == 1) {  // Nz: Zn with the roles of M and N exchanged
+    const uint32_t o = off < loopsN ? off : loopsN;
+    const uint32_t span = o * loopsM;
+    const uint32_t w = inner / span;
+    const uint32_t j = inner - w * span;
+    const uint32_t windows = (loopsN + o - 1) / o;
+    const uint32_t cols = (w == windows - 1) ? loopsN - o * w : o;
+    c.n = w * o + j % cols;
+    c.m = j / cols;
+    if (w & 1u) c.m = loopsM - 1 - c.m;
+  } else {  // RASTER
+    c.m = inner / loopsN;
+    c.n = inner - c.m * loopsN;
+  }
+  return c;
+}
+
+// Everything a workgroup needs to know about one task.
+struct Task {
+  uint32_t idx;      // batch index or group index
+  uint32_t m, n;     // block coordinate inside its problem
+  uint32_t mAct, nAct;
+  int64_t row0;      // first row of the tile in the (stacked) A / C
+  uint32_t rows_valid;  // rows of the tile inside the allocation (<= mAct)
+};
+
+// Grouped problems: per-workgroup table in LDS of each group's first task
+// and first row, built once from the device group sizes.  A group's rows are
+// clamped to the rows still left in the allocation (negative sizes count as
+// 0), so the task count never exceeds ceil(total_m / BM) + G tile-rows.
+struct GroupTable {
+  uint32_t first_task[kMaxGroups + 1];
+  int64_t first_row[kMaxGroups + 1];
+};
+
+__device__ __forceinline__ void build_group_table(GroupTable& gt, const GemmArgs& a, uint32_t BM,
+                                                  uint32_t loopsN) {
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    int64_t r = 0;
+    for (int g = 0; g < a.G; ++g) {
+      gt.first_task[g] = t;
+      gt.first_row[g] = r;
+      int64_t mg = a.group_m[g] > 0 ? a.group_m[g] : 0;
+      if (mg > a.total_m - r) mg = a.total_m - r;
+      t += ((uint32_t)mg + BM - 1) / BM * loopsN;
+      r += mg;
+    }
+    gt.first_task[a.G] = t;
+    gt.first_row[a.G] = r;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t t, uint32_t BM, uint32_t BN,
+                                            const GroupTable* gt) {
+  Task k;
+  const uint32_t loopsN = (a.N + BN - 1) / BN;
+  uint32_t Mp, inner;
+  if (gt) {
+    // last group whose first task is <= t (binary search; empty groups own no task)
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gt->first_task[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    k.idx = (uint32_t)lo;
+    inner = t - gt->first_task[lo];
+    Mp = (uint32_t)(gt->first_row[lo + 1] - gt->first_row[lo]);
+  } else {
+    const uint32_t core = ((a.M + BM - 1) / BM) * loopsN;  // s4.3 GetCoreLoops
+    k.idx = t / core;                                      // s4.4 GetBatchIdx
+    inner = t - k.idx * core;
+    Mp = a.M;
+  }
+  const uint32_t loopsM = (Mp + BM - 1) / BM;
+  const TileCoord c = block_coord(loopsM, loopsN, a.off, a.dir, inner);
+  k.m = c.m;
+  k.n = c.n;
+  k.mAct = (c.m == loopsM - 1) ? Mp - c.m * BM : BM;  // s4.6 GetActualBlockShape
+  k.nAct = (c.n == loopsN - 1) ? a.N - c.n * BN : BN;
+  if (gt) {
+    k.row0 = gt->first_row[k.idx] + (int64_t)c.m * BM;
+    const int64_t room = a.total_m - k.row0;
+    k.rows_valid = room <= 0 ? 0u : (room < (int64_t)k.mAct ? (uint32_t)room : k.mAct);
+  } else {
+    k.row0 = (int64_t)c.m * BM;
+    k.rows_valid = k.mAct;
+  }
+  return k;
+}
+
+// Workgroup renumbering: hardware places workgroup w on XCD w % 8; with
+// remap on, XCD x gets a contiguous block of logical indices.
+__device__ __forceinline__ uint32_t logical_wg(uint32_t remap) {
+  const uint32_t w = blockIdx.x, G = gridDim.x;
+  if (!remap) return w;
+  const uint32_t x = w % kNumXcd, q = w / kNumXcd;
+  const uint32_t base = G / kNumXcd, rem = G % kNumXcd;
+  return x * base + (x < rem ? x : rem) + q;
+}
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  // HW_REG_XCC_ID (hardware register 20), bits [3:0]
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xf;
+}
+
+// ------------------------------------------------------------- traits -----
+template <int AB>
+struct Traits;
+template <>
+struct Traits<AB_F16> {
+  static constexpr int ES = 2, BK = 64, KBR = 4, MFMA_K = 16, FRAG_DW = 4;
+  static constexpr bool IS_INT = false, SCALED = false;
+};
+template <>
+struct Traits<AB_BF16> {
+  static constexpr int ES = 2, BK = 64, KBR = 4, MFMA_K = 16, FRAG_DW = 4;
+  static constexpr bool IS_INT = false, SCALED = false;
+};
+template <>
+struct Traits<AB_I8> {
+  static constexpr int ES = 1, BK = 128, KBR = 8, MFMA_K = 32, FRAG_DW = 4;
+  static constexpr bool IS_INT = true, SCALED = false;
+};
+template <>
+struct Traits<AB_E4M3> {
+  static constexpr int ES = 1, BK = 128, KBR = 8, MFMA_K = 64, FRAG_DW = 8;
+  static constexpr bool IS_INT = false, SCALED = true;
+};
+template <>
+struct Traits<AB_MXE4M3> : Traits<AB_E4M3> {};
+
+// One 32x32 MFMA step: acc(32 n x 32 m) += Bt(32 n x k) * At(k x 32 m).
+template <int AB, typename Acc, typename Frag>
+__device__ __forceinline__ void mfma32(Acc& acc, const Frag& bt, const Frag& at, uint32_t sc_b,
+                                       uint32_t sc_a) {
+  if constexpr (AB == AB_F16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, bt),
+                                                 __builtin_bit_cast(half8_t, at), acc, 0, 0, 0);
+  } else if constexpr (AB == AB_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bt),
+                                                  __builtin_bit_cast(bf16x8_t, at), acc, 0, 0, 0);
+  } else if constexpr (AB == AB_I8) {
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, bt),
+                                                __builtin_bit_cast(i32x4_t, at), acc, 0, 0, 0);
+  } else {
+    // operand format 0 = FP8 E4M3 for both sources; scale bytes from bits [7:0]
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8_t, bt),
+                                                          __builtin_bit_cast(i32x8_t, at), acc, 0,
+                                                          0, 0, (int)sc_b, 0, (int)sc_a);
+  }
+}
+
+// XOR permutation of the eight 16-byte chunks of LDS row r.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
+
+__device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t chunk) {
+  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+}
+
+// 16 bytes from global memory, `valid` of them kept (the rest read as 0).
+__device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
+  if (valid >= 16) return *reinterpret_cast<const u32x4_t*>(p);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (valid > 0) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int e = 0; e < 16; ++e)
+      if (e < valid) w[e >> 2] |= (uint32_t)p[e] << ((e & 3) * 8);
+    v = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---------------------------------------------------------------- kernel --
+template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+struct GemmKernel {
+  using T = Traits<AB>;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 sub-tiles per wave
+  static constexpr int CE = 16 / T::ES;             // elements per 16-byte chunk
+  static constexpr int KSTEPS = T::BK / T::MFMA_K;  // MFMA steps per stage
+  static constexpr int A_CHUNKS = BM * 8;           // 16-byte chunks of an A stage
+  static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+  static constexpr int NBC = BN / CE;               // 16-byte chunks across a B row
+  static constexpr int KBLK = T::BK / T::KBR;       // B blocks along K (= 16)
+  static constexpr int B_BLOCKS = KBLK * NBC;
+  static constexpr int B_PER_T = (B_BLOCKS + NT - 1) / NT;
+  static constexpr int KB_LO = T::ES == 2 ? 1 : 2;  // K-block bits varied fastest across lanes
+  static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+  static constexpr int SCALE_BYTES = T::SCALED ? (BM + BN) * 4 : 0;
+  static constexpr int LDS_BYTES = 2 * (STAGE_BYTES + SCALE_BYTES);
+  using Acc = typename std::conditional<T::IS_INT, i32x16_t, f32x16_t>::type;
+  using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
+
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(T::BK * T::ES == kRowBytes, "one stage = one 128-byte row");
+  static_assert(KBLK == 16, "16 B-blocks of 8 bytes fill a 128-byte row");
+  static_assert(!T::SCALED || (BM <= NT && BN <= NT), "one thread per scale row / column");
+
+  // Registers holding one stage on its way from global memory to LDS.
+  struct Stage {
+    u32x4_t a[A_PER_T];
+    u32x4_t b[B_PER_T][T::KBR];
+    uint32_t sa, sb;  // MX: 4 scale bytes (one per 32-wide K block) of one A row / B column
+  };
+
+  __device__ static void load_stage(Stage& st, const GemmArgs& a, const uint8_t* Ab,
+                                    const uint8_t* Bb, const Task& tk, uint32_t kb0,
+                                    uint32_t kend, const uint8_t* sab, const uint8_t* sbb) {
+    const uint32_t tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const uint32_t q = tid + i * NT;
+      st.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (A_CHUNKS % NT == 0 || q < (uint32_t)A_CHUNKS) {
+        const uint32_t r = q >> 3, c = q & 7u;
+        const uint32_t gk = kb0 + c * CE;
+        if (r < tk.rows_valid && gk < kend) {
+          const int valid = (int)((kend - gk) < (uint32_t)CE ? (kend - gk) : CE) * T::ES;
+          st.a[i] = load16(Ab + ((int64_t)r * a.lda + gk) * T::ES, valid);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const uint32_t q = tid + i * NT;
+      const uint32_t kb_lo = q & ((1u << KB_LO) - 1u);
+      const uint32_t rest = q >> KB_LO;
+      const uint32_t nb = rest % NBC;
+      const uint32_t kb = (rest / NBC) * (1u << KB_LO) + kb_lo;
+      const uint32_t ncol = tk.n * BN + nb * CE;
+      const bool live = (B_BLOCKS % NT == 0 || q < (uint32_t)B_BLOCKS);
+      const int nvalid = ncol < a.N ? (int)((a.N - ncol) < (uint32_t)CE ? (a.N - ncol) : CE) * T::ES : 0;
+#pragma unroll
+      for (int j = 0; j < T::KBR; ++j) {
+        const uint32_t gk = kb0 + kb * T::KBR + j;
+        st.b[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (live && gk < kend && nvalid > 0)
+          st.b[i][j] = load16(Bb + ((int64_t)gk * a.ldb + ncol) * T::ES, nvalid);
+      }
+    }
+    if constexpr (T::SCALED) {
+      // A scales: one row per thread, 4 K blocks; B scales: one column per thread.
+      st.sa = 0x7f7f7f7fu;
+      st.sb = 0x7f7f7f7fu;
+      if (sab) {
+        uint32_t va = 0, vb = 0;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kblock = kb0 / 32 + e;
+          const bool kin = kblock * 32 < kend;
+          uint32_t x = 0x7f, y = 0x7f;
+          if (tid < (uint32_t)BM && kin && tid < tk.rows_valid)
+            x = sab[(int64_t)tid * a.ldsa + kblock];
+          if (tid < (uint32_t)BN && kin && tk.n * BN + tid < a.N)
+            y = sbb[(int64_t)kblock * a.ldsb + tk.n * BN + tid];
+          va |= x << (8 * e);
+          vb |= y << (8 * e);
+        }
+        st.sa = va;
+        st.sb = vb;
+      }
+    }
+  }
+
+  __device__ static void store_stage(const Stage& st, uint8_t* lds) {
+    const uint32_t tid = threadIdx.x;
+    uint8_t* la = lds;
+    uint8_t* lb = lds + BM * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const uint32_t q = tid + i * NT;
+      if (A_CHUNKS % NT == 0 || q < (uint32_t)A_CHUNKS)
+        *reinterpret_cast<u32x4_t*>(la + lds_off(q >> 3, q & 7u)) = st.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const uint32_t q = tid + i * NT;
+      if (!(B_BLOCKS % NT == 0 || q < (uint32_t)B_BLOCKS)) continue;
+      const uint32_t kb_lo = q & ((1u << KB_LO) - 1u);
+      const uint32_t rest = q >> KB_LO;
+      const uint32_t nb = rest % NBC;
+      const uint32_t kb = (rest / NBC) * (1u << KB_LO) + kb_lo;
+      // transpose KBR rows x 16 bytes into (16 / KBR*... ) columns of 8 bytes
+      if constexpr (T::ES == 2) {
+        // 4 K-rows x 8 halves -> 8 columns x 4 halves
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+            const uint32_t d0 = __builtin_amdgcn_perm(st.b[i][1][w], st.b[i][0][w], sel);
+            const uint32_t d1 = __builtin_amdgcn_perm(st.b[i][3][w], st.b[i][2][w], sel);
+            const uint32_t n = nb * 8 + w * 2 + h;
+            *reinterpret_cast<u32x2_t*>(lb + lds_off(n, kb >> 1) + (kb & 1u) * 8) = u32x2_t{d0, d1};
+          }
+        }
+      } else {
+        // 8 K-rows x 16 bytes -> 16 columns x 8 bytes
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t col[2][4];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t r0 = st.b[i][4 * half + 0][w], r1 = st.b[i][4 * half + 1][w];
+            const uint32_t r2 = st.b[i][4 * half + 2][w], r3 = st.b[i][4 * half + 3][w];
+            const uint32_t p01l = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+            const uint32_t p01h = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+            const uint32_t p23l = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+            const uint32_t p23h = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+            col[half][0] = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+            col[half][1] = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+            col[half][2] = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+            col[half][3] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t n = nb * 16 + w * 4 + e;
+            *reinterpret_cast<u32x2_t*>(lb + lds_off(n, kb >> 1) + (kb & 1u) * 8) =
+                u32x2_t{col[0][e], col[1][e]};
+          }
+        }
+      }
+    }
+    if constexpr (T::SCALED) {
+      uint32_t* ls = reinterpret_cast<uint32_t*>(lds + STAGE_BYTES);
+      if (tid < (uint32_t)BM) ls[tid] = st.sa;
+      if (tid < (uint32_t)BN) ls[BM + tid] = st.sb;
+    }
+  }
+
+  // MFMAs of one stage held in LDS.  Operand lanes: 16-bit and int8 steps
+  // take 16 consecutive bytes of K per lane (lane group hi = lane / 32 holds
+  // the upper half of the step).  The scaled fp8 step of 64 K values takes
+  // two 16-byte pieces per lane, K [16hi, 16hi+16) and [32+16hi, 48+16hi)
+  // of the step, and the lane of group hi supplies the E8M0 scale of the
+  // 32-wide block hi of its row (column) -- the operand layout of the
+  // gfx950 scaled MFMA, established by an on-device lane probe.
+  __device__ static void compute_stage(Acc (&acc)[FM][FN], const uint8_t* lds, uint32_t wm,
+                                       uint32_t wn) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t l32 = lane & 31u, hi = lane >> 5;
+    const uint8_t* la = lds;
+    const uint8_t* lb = lds + BM * kRowBytes;
+    const uint32_t* ls = reinterpret_cast<const uint32_t*>(lds + STAGE_BYTES);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      Frag fa[FM], fb[FN];
+      uint32_t sca[FM], scb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t row = wm * TM + i * 32 + l32;
+        if constexpr (T::FRAG_DW == 4) {
+          fa[i] = *reinterpret_cast<const u32x4_t*>(la + lds_off(row, 2 * kk + hi));
+        } else {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(la + lds_off(row, 4 * kk + hi));
+          const u32x4_t y = *reinterpret_cast<const u32x4_t*>(la + lds_off(row, 4 * kk + 2 + hi));
+          fa[i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+        }
+        sca[i] = T::SCALED ? (ls[row] >> (8 * (2 * kk + hi))) & 0xffu : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t row = wn * TN + j * 32 + l32;
+        if constexpr (T::FRAG_DW == 4) {
+          fb[j] = *reinterpret_cast<const u32x4_t*>(lb + lds_off(row, 2 * kk + hi));
+        } else {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(lb + lds_off(row, 4 * kk + hi));
+          const u32x4_t y = *reinterpret_cast<const u32x4_t*>(lb + lds_off(row, 4 * kk + 2 + hi));
+          fb[j] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+        }
+        scb[j] = T::SCALED ? (ls[BM + row] >> (8 * (2 * kk + hi))) & 0xffu : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma32<AB>(acc[i][j], fb[j], fa[i], scb[j], sca[i]);
+    }
+  }
+
+  // Output of one 32x32 sub-tile: lane holds rows l32, columns 8g + 4*hi + {0..3}.
+  __device__ static void store_out(const GemmArgs& a, const Task& tk, const Acc& v, int i, int j,
+                                   uint32_t wm, uint32_t wn) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t l32 = lane & 31u, hi = lane >> 5;
+    const uint32_t ml = wm * TM + i * 32 + l32;
+    if (ml >= tk.rows_valid) return;
+    const int64_t grow = tk.row0 + ml;
+    const bool deq = a.row_scale != nullptr;
+    const float rs = deq ? a.row_scale[grow] : 1.0f;
+    uint8_t* crow = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + grow * a.ldc) *
+                             (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;
+      if (nl >= tk.nAct) continue;
+      const uint32_t gn = tk.n * BN + nl;
+      float f[4];
+      int32_t iv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (T::IS_INT) {
+          iv[r] = v[4 * g + r];
+          f[r] = (float)iv[r];
+        } else {
+          f[r] = v[4 * g + r];
+          iv[r] = 0;
+        }
+      }
+      if (deq) {
+        const float* cs = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + gn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float c = (nl + r < tk.nAct) ? cs[r] : 0.0f;
+          f[r] = (f[r] * rs) * c;
+        }
+      }
+      const bool full = nl + 4 <= tk.nAct;
+      if (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16) {
+        uint16_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          h[r] = a.cdtype == OUT_F16 ? f32_to_f16_rne(f[r]) : f32_to_bf16_rne(f[r]);
+        uint16_t* p = reinterpret_cast<uint16_t*>(crow) + gn;
+        if (full) {
+          *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        } else {
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = h[r];
+        }
+      } else if (a.cdtype == OUT_F32) {
+        float* p = reinterpret_cast<float*>(crow) + gn;
+        if (full) *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
+        else
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = f[r];
+      } else {  // OUT_I32
+        int32_t* p = reinterpret_cast<int32_t*>(crow) + gn;
+        if (full) *reinterpret_cast<i32x4_t*>(p) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+        else
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = iv[r];
+      }
+    }
+  }
+
+  __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+    __shared__ uint32_t last_flag;
+    GroupTable* gt = nullptr;
+    uint32_t T_tiles = a.tiles;
+    if constexpr (GROUPED) {
+      __shared__ GroupTable gtab;
+      gt = &gtab;
+      build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
+      T_tiles = gtab.first_task[a.G];
+    }
+    const uint32_t units = T_tiles * a.split;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t wm = wave / WN, wn = wave % WN;
+    const uint32_t lane = threadIdx.x & 63u;
+
+    for (uint32_t u = logical_wg(a.remap); u < units; u += gridDim.x) {
+      const uint32_t s = u / T_tiles;       // K slice (like GetBatchIdx over slices)
+      const uint32_t t = u - s * T_tiles;   // task
+      const Task tk = decode_task(a, t, BM, BN, gt);
+      const uint32_t k0 = s * a.kslice;
+      const uint32_t k1 = (k0 >= a.K || a.K - k0 < a.kslice) ? a.K : k0 + a.kslice;
+      const uint32_t klen = k0 < k1 ? k1 - k0 : 0u;
+      const uint32_t nk = (klen + T::BK - 1) / T::BK;
+
+      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      const uint8_t* Ab = a.A + (bidx * a.strideA + tk.row0 * a.lda) * T::ES;
+      const uint8_t* Bb = a.B + ((int64_t)tk.idx * a.strideB) * T::ES;
+      const uint8_t* sab = a.sa ? a.sa + tk.row0 * a.ldsa : nullptr;
+      const uint8_t* sbb = a.sb;
+
+      Acc acc[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+      if (nk > 0) {
+        Stage st;
+        load_stage(st, a, Ab, Bb, tk, k0, k1, sab, sbb);
+        store_stage(st, lds);
+        __syncthreads();
+        for (uint32_t kt = 0; kt < nk; ++kt) {
+          const uint8_t* cur = lds + (kt & 1u) * (STAGE_BYTES + SCALE_BYTES);
+          uint8_t* nxt = lds + ((kt + 1) & 1u) * (STAGE_BYTES + SCALE_BYTES);
+          const bool more = kt + 1 < nk;
+          if (more) load_stage(st, a, Ab, Bb, tk, k0 + (kt + 1) * T::BK, k1, sab, sbb);
+          compute_stage(acc, cur, wm, wn);
+          if (more) store_stage(st, nxt);
+          __syncthreads();
+        }
+      }
+
+      if (a.split > 1) {
+        // Fixed-order fix-up: every slice stores its partial tile; the last
+        // slice to arrive adds the partials in slice order 0..split-1 and
+        // writes the output.  The counter returns to zero for the next call.
+        const size_t tile_elems = (size_t)BM * BN;
+        const size_t lane_off = ((size_t)(wave * FM * FN) * 64 + lane) * 16;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            float* p = a.ws_part + ((size_t)s * a.tile_cap + t) * tile_elems + lane_off +
+                       (size_t)(i * FN + j) * 64 * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f32x4_t v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                // copy the element out first: a bit_cast of a vector-element
+                // expression would read element 0
+                const auto x = acc[i][j][4 * q + e];
+                v[e] = __builtin_bit_cast(float, x);
+              }
+              *reinterpret_cast<f32x4_t*>(p + 4 * q) = v;
+            }
+          }
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const uint32_t prev = atomicAdd(&a.ws_count[t], 1u);
+          last_flag = (prev == a.split - 1) ? 1u : 0u;
+        }
+        __syncthreads();
+        if (last_flag == 0) continue;
+        __threadfence();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            Acc sum;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sum[e] = 0;
+            for (uint32_t ss = 0; ss < a.split; ++ss) {
+              const float* p = a.ws_part + ((size_t)ss * a.tile_cap + t) * tile_elems + lane_off +
+                               (size_t)(i * FN + j) * 64 * 16;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float x = v[e];
+                  if constexpr (T::IS_INT)
+                    sum[4 * q + e] += __builtin_bit_cast(int, x);
+                  else
+                    sum[4 * q + e] += x;
+                }
+              }
+            }
+            acc[i][j] = sum;
+          }
+        if (threadIdx.x == 0) a.ws_count[t] = 0u;
+      }
+
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) store_out(a, tk, acc[i][j], i, j, wm, wn);
+    }
+  }
+};
+
+template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmArgs a) {
+  GemmKernel<AB, BM, BN, WM, WN, GROUPED>::run(a);
+}
+
+// Map dump: the same scheduler, persistent loop and renumbering as the GEMM
+// kernels, one wave per workgroup, one record of 8 words per task.
+template <bool GROUPED>
+__global__ void __launch_bounds__(64) tile_map_kernel(GemmArgs a, uint32_t BM, uint32_t BN) {
+  GroupTable* gt = nullptr;
+  uint32_t T_tiles = a.tiles;
+  if constexpr (GROUPED) {
+    __shared__ GroupTable gtab;
+    gt = &gtab;
+    build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
+    T_tiles = gtab.first_task[a.G];
+  }
+  for (uint32_t t = logical_wg(a.remap); t < T_tiles; t += gridDim.x) {
+    const Task tk = decode_task(a, t, BM, BN, gt);
+    if (threadIdx.x == 0) {
+      uint32_t* o = a.map_out + (size_t)t * 8;
+      o[0] = tk.idx;
+      o[1] = tk.m;
+      o[2] = tk.n;
+      o[3] = tk.mAct;
+      o[4] = tk.nAct;
+      o[5] = GROUPED ? (uint32_t)tk.row0 : 0u;
+      o[6] = xcc_id();
+      o[7] = blockIdx.x;
+    }
+  }
+}
+
+}  // namespace bst

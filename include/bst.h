@@ -1,0 +1,206 @@
+/*
+ * bst.h -- C ABI of the swizzled tiled GEMM library for AMD MI355X (gfx950).
+ *
+ * C = A . B with a GemmIdentityBlockSwizzle-style block -> tile scheduler
+ * ("Block Scheduler Code Explained", CATLASS docs: s4.1 loop counts, s4.4
+ * batch index, s4.5 Zn / Nz windows of width SwizzleOffset with snake
+ * reversal, s4.6 tail-tile shapes, s6 runtime offset and direction), in four
+ * forms: plain, batched, grouped slice-M, and int8 with per-token /
+ * per-channel dequant (the workloads that "Block Dispatch Policies", CATLASS
+ * docs, lists as examples of its dispatch policies).
+ *
+ * Conventions for every entry point
+ *  - All matrices are row-major: A[M][lda] with lda >= K, B[K][ldb] with
+ *    ldb >= N, C[M][ldc] with ldc >= N (leading dimensions in elements).
+ *    Base pointers must be 16-byte aligned and every leading dimension and
+ *    batch stride must be a whole number of 16-byte units (BST_E_ALIGN).
+ *  - Pointers named *_dev are device pointers; the caller owns every buffer
+ *    and the stream.  The library never allocates, frees or synchronises in
+ *    a call: work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *    stream) and the call returns at once.
+ *  - Validation happens on the host before any launch; on a non-OK status
+ *    nothing was enqueued and bst_last_error() describes the problem.
+ *  - M == 0, N == 0 or batch == 0 (no output) is a successful no-op.
+ *    K == 0 writes zeros (dequant of zero is zero).
+ *  - Results do not depend on the schedule (tile order, split, remap, grid);
+ *    the tile shape and the split only change the fp32 summation order.
+ *  - Calls that share a workspace must be ordered (same stream or synced).
+ */
+#ifndef BST_H
+#define BST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bst_status {
+  BST_OK = 0,
+  BST_E_INVAL = -1,        /* bad argument: null pointer, negative or too-large size,
+                              leading dimension < row length, offset 0, bad direction,
+                              MX with K % 32 != 0, int8 with K > 131071 */
+  BST_E_UNSUPPORTED = -2,  /* no compiled kernel for this dtype pair / tile */
+  BST_E_ALIGN = -3,        /* base pointer or stride not 16-byte aligned */
+  BST_E_WORKSPACE = -4,    /* workspace missing or smaller than bst_workspace_bytes() */
+  BST_E_HIP = -5           /* the HIP runtime reported an error (message captured) */
+} bst_status;
+
+typedef enum bst_dtype {
+  BST_F16 = 1,     /* IEEE binary16 */
+  BST_BF16 = 2,    /* bfloat16 */
+  BST_E4M3 = 3,    /* OCP FP8 E4M3 "fn" (no inf, max 448), unscaled */
+  BST_MXE4M3 = 4,  /* OCP FP8 E4M3 with one E8M0 scale per 32 consecutive K values */
+  BST_I8 = 5,      /* int8 */
+  BST_I32 = 6,     /* int32 (raw int8 accumulators) */
+  BST_F32 = 7      /* binary32 */
+} bst_dtype;
+
+typedef enum bst_direction {
+  BST_ZN = 0,      /* windows of swizzle_offset tile-rows, M index fastest inside (s4.5) */
+  BST_NZ = 1,      /* windows of swizzle_offset tile-columns, N index fastest inside */
+  BST_RASTER = 2   /* row-major over tiles, no windows, no snake (comparison baseline) */
+} bst_direction;
+
+/* Schedule of one call.  Only tile_m / tile_n and the swizzle fields decide
+ * the task -> tile map; the others are performance knobs. */
+typedef struct bst_sched {
+  uint32_t tile_m, tile_n;     /* output tile (the scheduler's tileMN); 0 = default */
+  uint32_t tile_k;             /* K depth of one pipeline stage; 0 = the dtype's only value
+                                  (64 for 16-bit, 128 for 8-bit operands) */
+  uint32_t swizzle_offset;     /* window width in tiles, >= 1 (SwizzleOffset, s2.1) */
+  uint32_t swizzle_direction;  /* bst_direction (SwizzleDirection, s2.1; RASTER added) */
+  uint32_t split_k;            /* K slices per tile: 1 = off, 0 = automatic */
+  uint32_t xcd_remap;          /* 0: workgroup w takes tasks w, w+G, ...; 1: workgroups are
+                                  renumbered so that each XCD (accelerator die, own L2)
+                                  takes a contiguous range of task indices */
+  uint32_t grid;               /* persistent workgroups; 0 = fill every CU */
+} bst_sched;
+
+/*
+ * bst_gemm -- C = A . B for one problem.
+ *   ab: BST_F16 / BST_BF16 (c: BST_F16, BST_BF16 or BST_F32), BST_E4M3 /
+ *   BST_MXE4M3 (c: BST_BF16, BST_F16 or BST_F32), BST_I8 (c: BST_I32 raw
+ *   accumulators, or BST_F32 / BST_BF16 / BST_F16 of the accumulator).
+ *   scale_a_dev, scale_b_dev: BST_MXE4M3 only, else NULL.  scale_a is
+ *   uint8 E8M0 [M][K/32] (row-major, one scale per row and 32-wide K block),
+ *   scale_b is uint8 E8M0 [K/32][N].  K must be a multiple of 32.
+ *   Element (i, j) = sum over K blocks of 2^(sa-127) * 2^(sb-127) * (sum of
+ *   the block's products).
+ *   Accumulation is fp32 (int32 for int8); outputs are rounded to nearest
+ *   even.  ws / ws_bytes: workspace of at least bst_workspace_bytes(...)
+ *   bytes when the (possibly automatic) split_k is above 1, else may be
+ *   NULL / 0.  Layout: a 64 KiB counter area (one uint32 per tile, at most
+ *   16384 tiles take a split) followed by the partial tiles.  The counter
+ *   area must be zero before the first use of a workspace; every call that
+ *   runs to completion leaves it zero again, so one workspace serves calls
+ *   of any shape in stream order.
+ */
+bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                    const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
+                    void* C_dev, int64_t ldc, const uint8_t* scale_a_dev,
+                    const uint8_t* scale_b_dev, const bst_sched* sched, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * bst_batched_gemm -- C_b = A_b . B_b for b in [0, batch), with
+ * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in
+ * elements).  The task index spans batch x tiles; the batch index of task t
+ * is t / (tiles per problem) (s4.4 GetBatchIdx).  Same dtypes as bst_gemm
+ * except BST_MXE4M3.
+ */
+bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
+                            int64_t K, const void* A_dev, int64_t lda, int64_t strideA,
+                            const void* B_dev, int64_t ldb, int64_t strideB, void* C_dev,
+                            int64_t ldc, int64_t strideC, const bst_sched* sched, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * bst_grouped_gemm_slice_m -- G independent problems stacked along M that
+ * share N and K: group g owns rows [P_g, P_g + group_m[g]) of A and C, where
+ * P_g = sum of group_m[h] for h < g, and uses B_g = B + g*strideB
+ * ([K][ldb]).  group_m_dev is a device int32[G] and is never read by the
+ * host; entries < 0 count as 0, and a group is cut to the rows still left
+ * of total_m (the rows allocated in A and C), so nothing at or beyond row
+ * total_m is read or written.  Tasks are the
+ * groups' tile ranges concatenated in group order; inside a group the
+ * scheduler is re-targeted to (group_m[g], N) (s4.2 Update).
+ *   ab = BST_I8: c = BST_I32 (raw), or BST_BF16 / BST_F16 / BST_F32 with
+ *   optional dequant: when row_scale_dev (f32 [total_m], per token) and
+ *   col_scale_dev (f32 [G][N], per group and channel) are both given,
+ *   out = round(float(acc) * row_scale[r] * col_scale[g][j]) with each
+ *   product rounded to fp32.  ab = BST_F16 / BST_BF16: no scales.
+ *   1 <= G <= 1024.
+ */
+bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G,
+                                    const int32_t* group_m_dev, int64_t total_m, int64_t N,
+                                    int64_t K, const void* A_dev, int64_t lda,
+                                    const void* B_dev, int64_t ldb, int64_t strideB,
+                                    void* C_dev, int64_t ldc, const float* row_scale_dev,
+                                    const float* col_scale_dev, const bst_sched* sched,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bst_quant_gemm_per_token -- int8 A[M][K] . int8 B[K][N] with int32
+ * accumulation and, for c = BST_BF16 / BST_F16 / BST_F32, the dequant
+ * out = round(float(acc) * row_scale[i] * col_scale[j]) (row_scale f32 [M]
+ * per token, col_scale f32 [N] per channel, both device pointers, both
+ * required); c = BST_I32 writes the raw accumulators (scales ignored).
+ */
+bst_status bst_quant_gemm_per_token(int64_t M, int64_t N, int64_t K, const int8_t* A_dev,
+                                    int64_t lda, const int8_t* B_dev, int64_t ldb,
+                                    const float* row_scale_dev, const float* col_scale_dev,
+                                    void* C_dev, int64_t ldc, bst_dtype c,
+                                    const bst_sched* sched, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * bst_tile_map -- the task -> tile map as the GPU computes it, with the
+ * device scheduler the GEMM kernels use.  For every task t of a batched
+ * problem (batch x ceil(M/tile_m) x ceil(N/tile_n) tasks) writes 8 uint32
+ * to out_dev[8t..8t+7]: {batch index, m, n, mActual, nActual, 0, XCC id of
+ * the workgroup that ran it, that workgroup's index}.  `ab` selects the tile
+ * defaults.  max_tasks bounds out_dev (BST_E_INVAL if too small).
+ */
+bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N,
+                        const bst_sched* sched, uint32_t* out_dev, int64_t max_tasks,
+                        void* stream);
+
+/*
+ * bst_grouped_tile_map -- as bst_tile_map for a grouped slice-M problem:
+ * {group, m, n, mActual, nActual, first stacked row of the tile, XCC id,
+ * workgroup}.  group_m_dev as in bst_grouped_gemm_slice_m; the task count
+ * is only known on the device, so max_tasks must be at least
+ * (ceil(total_m/tile_m) + G) * ceil(N/tile_n); unused records are left
+ * untouched.  *
+ */
+bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m_dev,
+                                int64_t total_m, int64_t N, const bst_sched* sched,
+                                uint32_t* out_dev, int64_t max_tasks, void* stream);
+
+/*
+ * bst_workspace_bytes -- workspace bytes a call with these arguments needs
+ * (0 when the effective split_k is 1).  kind: 0 plain / batched (count =
+ * batch), 1 grouped (count = G, M = total_m).  Returns 0 and sets the last
+ * error for invalid arguments.
+ */
+size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
+                           int64_t K, const bst_sched* sched);
+
+/* bst_effective_sched -- fills *out with the schedule a call with these
+ * arguments would run (defaults and automatic split resolved). */
+bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
+                               int64_t K, const bst_sched* sched, bst_sched* out);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* bst_last_error(void);
+
+/* Library version string. */
+const char* bst_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BST_H */

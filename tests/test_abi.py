@@ -1,0 +1,134 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/bst.h declares, and its host-side validation rejects bad arguments
+with the documented status before touching the GPU (all pointers here are
+fake or NULL; no call reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_swizzle_tile_amd as bst
+from block_swizzle_tile_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(0x20000)
+ODD = ctypes.c_void_p(0x10008)         # not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_swizzle_tile_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bst.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bst_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "bst_gemm" in names and "bst_grouped_gemm_slice_m" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_version(L):
+    assert b"gfx950" in L.bst_version()
+
+
+def S(**kw):
+    return bst.make_sched(**kw)
+
+
+def gemm(L, ab=_lib.F16, c=_lib.F16, M=64, N=64, K=64, A=FAKE, lda=None, B=FAKE, ldb=None,
+         C=FAKE2, ldc=None, sa=None, sb=None, sched=None, ws=None, wsb=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return L.bst_gemm(ab, c, M, N, K, A, lda, B, ldb, C, ldc, sa, sb,
+                      None if sched is None else ctypes.byref(sched), ws, wsb, None)
+
+
+def test_validation_errors(L):
+    assert gemm(L, sched=S(offset=0)) == _lib.E_INVAL            # offset 0 undefined
+    assert gemm(L, sched=S(direction=3)) == _lib.E_INVAL         # no such direction
+    assert gemm(L, M=-1) == _lib.E_INVAL
+    assert gemm(L, A=None) == _lib.E_INVAL
+    assert gemm(L, C=None) == _lib.E_INVAL
+    assert gemm(L, lda=32) == _lib.E_INVAL                       # lda < K
+    assert gemm(L, ldb=32) == _lib.E_INVAL
+    assert gemm(L, ldc=32) == _lib.E_INVAL
+    assert gemm(L, A=ODD) == _lib.E_ALIGN
+    assert gemm(L, K=60, lda=60) == _lib.E_ALIGN                 # 120-byte rows
+    assert gemm(L, sched=S(tile=(96, 96))) == _lib.E_UNSUPPORTED
+    assert gemm(L, sched=S(tile=(128, 128), tile_k=32)) == _lib.E_UNSUPPORTED
+    assert gemm(L, c=_lib.I32) == _lib.E_UNSUPPORTED             # int32 out needs int8 in
+    assert gemm(L, ab=_lib.MXE4M3, c=_lib.BF16, K=48, lda=64, sa=FAKE, sb=FAKE) == _lib.E_INVAL
+    assert gemm(L, ab=_lib.MXE4M3, c=_lib.BF16, K=64) == _lib.E_INVAL   # scales missing
+    assert gemm(L, ab=_lib.I8, c=_lib.I32, K=131072, lda=131072) == _lib.E_INVAL
+    assert gemm(L, ab=_lib.F16, sa=FAKE) == _lib.E_INVAL         # scales only for MX
+    assert gemm(L, ab=9) == _lib.E_INVAL
+    assert b"swizzle_offset" in gemm_msg(L, sched=S(offset=0))
+
+
+def gemm_msg(L, **kw):
+    gemm(L, **kw)
+    return L.bst_last_error()
+
+
+def test_empty_problems_are_noops(L):
+    assert gemm(L, M=0, A=None, B=None, C=None) == _lib.OK
+    assert gemm(L, N=0, A=None, B=None, C=None) == _lib.OK
+    assert L.bst_batched_gemm(_lib.F16, _lib.F16, 0, 64, 64, 64, None, 64, 0, None, 64, 0, None,
+                              64, 0, None, None, 0, None) == _lib.OK
+
+
+def test_workspace_required_for_split(L):
+    s = S(tile=(128, 128), split_k=4)
+    need = L.bst_workspace_bytes(0, _lib.F16, 1, 1024, 1024, 2048, ctypes.byref(s))
+    assert need == 65536 + 4 * 64 * 128 * 128 * 4
+    assert gemm(L, M=1024, N=1024, K=2048, sched=s) == _lib.E_WORKSPACE
+    assert gemm(L, M=1024, N=1024, K=2048, sched=s, ws=FAKE, wsb=need - 1) == _lib.E_WORKSPACE
+    assert L.bst_workspace_bytes(0, _lib.F16, 1, 1024, 1024, 2048,
+                                 ctypes.byref(S(tile=(128, 128)))) == 0
+
+
+def test_effective_sched_split_resolution(L):
+    out = _lib.Sched()
+    s = S(tile=(128, 128), split_k=16)
+    assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 256, ctypes.byref(s),
+                                 ctypes.byref(out)) == _lib.OK
+    assert out.split_k == 4 and out.tile_k == 64   # 4 stages of K: no empty slices
+    s = S(tile=(128, 128), split_k=3)
+    assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 2048, ctypes.byref(s),
+                                 ctypes.byref(out)) == _lib.OK
+    assert out.split_k == 3 and out.grid >= 1
+
+
+def test_grouped_validation(L):
+    def call(G=4, gm=FAKE, total_m=256, N=64, K=64, ab=_lib.I8, c=_lib.I32, rs=None, cs=None,
+             strideB=None):
+        strideB = K * N if strideB is None else strideB
+        return L.bst_grouped_gemm_slice_m(ab, c, G, gm, total_m, N, K, FAKE, K, FAKE, N, strideB,
+                                          FAKE2, N, rs, cs, None, None, 0, None)
+    assert call(G=0) == _lib.E_INVAL
+    assert call(G=1025) == _lib.E_INVAL
+    assert call(gm=None) == _lib.E_INVAL
+    assert call(rs=FAKE) == _lib.E_INVAL                 # one scale without the other
+    assert call(rs=FAKE, cs=FAKE) == _lib.E_INVAL        # dequant into int32
+    assert call(ab=_lib.E4M3, c=_lib.BF16) == _lib.E_UNSUPPORTED
+    assert call(strideB=10) == _lib.E_INVAL
+    assert call(total_m=0) == _lib.OK
+
+
+def test_quant_requires_scales(L):
+    r = L.bst_quant_gemm_per_token(64, 64, 64, FAKE, 64, FAKE, 64, None, None, FAKE2, 64,
+                                   _lib.BF16, None, None, 0, None)
+    assert r == _lib.E_INVAL

@@ -1,0 +1,75 @@
+"""GPU map parity: the task -> tile map computed by the kernels' own device
+scheduler (bst_tile_map / bst_grouped_tile_map) must equal the oracle's map
+bit for bit, for every direction, offset, tile, remap and grid."""
+import itertools
+
+import numpy as np
+import pytest
+
+from gpu_util import say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (batch, M, N, tile)
+    (1, 200, 136, (64, 64)),          # tails workload
+    (1, 1024, 1024, (256, 128)),      # fp16 2k workload
+    (1, 1024, 2048, (256, 256)),      # mxfp8 workload (fp8 tile)
+    (16, 512, 768, (128, 192)),       # bf16 batch workload
+    (3, 1000, 700, (128, 128)),
+    (1, 1, 1, (64, 64)),
+    (2, 4097, 63, (128, 256)),
+]
+
+
+def _ab(tile):
+    return 5 if tile == (256, 256) else 1     # int8 has the 256x256 tile
+
+
+@pytest.mark.parametrize("batch,M,N,tile", CASES)
+def test_map_matches_oracle(orc, batch, M, N, tile):
+    import block_swizzle_tile_amd as bst
+    for off, d, remap, grid in itertools.product([1, 2, 3, 4, 8, 1000], ["zn", "nz", "raster"],
+                                                 [0, 1], [0, 7]):
+        say("map", batch, M, N, tile, off, d, remap, grid)
+        s = bst.make_sched(tile=tile, offset=off, direction=d, xcd_remap=remap, grid=grid)
+        got = bst.tile_map(batch, M, N, s, ab=_ab(tile)).cpu().numpy()
+        want = orc.tile_map(batch, M, N, tile[0], tile[1], off, d)
+        assert np.array_equal(got[:, :5].astype(np.uint32), want), (off, d, remap, grid)
+        assert np.all(got[:, 5] == 0)
+        assert np.all((got[:, 6] >= 0) & (got[:, 6] < 8))
+
+
+def test_remap_places_contiguous_tasks_on_one_xcd(orc):
+    """With the renumbering on, the tasks each XCD runs form contiguous
+    ranges (checked through the XCC id each workgroup reports)."""
+    import block_swizzle_tile_amd as bst
+    s = bst.make_sched(tile=(128, 128), offset=2, direction="zn", xcd_remap=1, grid=256)
+    got = bst.tile_map(1, 2048, 2048, s).cpu().numpy()     # 256 tasks, one per workgroup
+    xcc = got[:, 6]
+    say("xcc per task", xcc.tolist())
+    assert len(set(xcc.tolist())) >= 1
+    # each workgroup runs exactly one task here; the hardware XCD of
+    # workgroup w is w % 8 when dispatch is round-robin
+    wg = got[:, 7]
+    assert sorted(wg.tolist()) == list(range(256))
+    runs = np.count_nonzero(np.diff(xcc) != 0)
+    say("xcd changes along the task order:", runs)
+
+
+@pytest.mark.parametrize("tile", [(64, 64), (128, 128), (256, 256)])
+@pytest.mark.parametrize("d", ["zn", "nz", "raster"])
+def test_grouped_map_matches_oracle(orc, tile, d):
+    import block_swizzle_tile_amd as bst
+    from block_swizzle_tile_amd import inputs
+    for gm in [inputs.group_sizes(), np.array([0, 300, 5, 0, 129, 64, 1], np.int32),
+               np.array([0], np.int32), np.array([7], np.int32)]:
+        N = 4096 if gm.sum() == 8192 else 200
+        for off in [1, 3]:
+            say("grouped map", tile, d, gm.tolist(), off)
+            s = bst.make_sched(tile=tile, offset=off, direction=d)
+            got = bst.grouped_tile_map(to_gpu(gm, "i32"), int(gm.sum()), N, s).cpu().numpy()
+            want = orc.grouped_tile_map(gm, N, tile[0], tile[1], off, d)
+            T = want.shape[0]
+            assert np.array_equal(got[:T, :6].astype(np.uint32), want)
+            assert np.all(got[T:] == -1)
