@@ -7,12 +7,15 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "bst.hip")
-DEPS = [SRC, os.path.join(PKG, "csrc", "bst_device.hpp"), os.path.join(ROOT, "include", "bst.h")]
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["bst.hip", "inst_f16.hip", "inst_bf16.hip", "inst_i8.hip", "inst_fp8.hip"]
+HEADERS = ["bst_device.hpp", "bst_kernel_dma.hpp", "bst_instances.hpp"]
+DEPS = ([os.path.join(CSRC, f) for f in SOURCES + HEADERS] +
+        [os.path.join(ROOT, "include", "bst.h")])
 LIB = os.path.join(PKG, "libbst.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-pass-failed",
 ]
@@ -24,17 +27,34 @@ def build(force: bool = True, verbose: bool = False) -> str:
             os.path.getmtime(LIB) >= os.path.getmtime(d) for d in DEPS):
         return LIB
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    for src in SOURCES:     # one process per translation unit, in parallel
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = ([hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-c",
+                                        os.path.join(CSRC, src), "-o", obj])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+    objs, failed = [], False
+    for obj, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out)
+            failed = True
+        objs.append(obj)
+    if failed:
+        raise RuntimeError("hipcc failed building libbst.so")
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libbst.so")
+        raise RuntimeError("linking libbst.so failed")
     os.replace(tmp, LIB)
     return LIB
-
 
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -12,7 +12,7 @@
 #include <unordered_map>
 
 #include "bst.h"
-#include "bst_device.hpp"
+#include "bst_instances.hpp"
 
 using namespace bst;
 
@@ -28,65 +28,18 @@ bst_status fail(bst_status st, const char* fmt, ...) {
   return st;
 }
 
-// ------------------------------------------------------------ instances ---
-using LaunchFn = hipError_t (*)(dim3, dim3, hipStream_t, const GemmArgs&);
-
-struct Instance {
-  int ab;  // AbKind (AB_MXE4M3 shares the AB_E4M3 kernels)
-  int bm, bn;
-  bool grouped;
-  const void* fn;
-  LaunchFn launch;
-  int threads;
-  int bk;
-};
-
-template <int AB, int BM, int BN, int WM, int WN, bool GR>
-hipError_t launch_impl(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
-  hipLaunchKernelGGL((gemm_kernel<AB, BM, BN, WM, WN, GR>), grid, block, 0, st, a);
-  return hipGetLastError();
-}
-
-#define BST_INST(AB, BM, BN, WM, WN, GR)                                                  \
-  Instance {                                                                              \
-    AB, BM, BN, GR, reinterpret_cast<const void*>(&gemm_kernel<AB, BM, BN, WM, WN, GR>), \
-        &launch_impl<AB, BM, BN, WM, WN, GR>, 64 * WM * WN, Traits<AB>::BK                \
-  }
-
-const Instance kInstances[] = {
-    BST_INST(AB_F16, 64, 64, 2, 2, false),
-    BST_INST(AB_F16, 128, 128, 2, 2, false),
-    BST_INST(AB_F16, 256, 128, 2, 2, false),
-    BST_INST(AB_F16, 128, 256, 2, 2, false),
-    BST_INST(AB_F16, 128, 192, 2, 2, false),
-    BST_INST(AB_F16, 128, 128, 2, 2, true),
-    BST_INST(AB_BF16, 64, 64, 2, 2, false),
-    BST_INST(AB_BF16, 128, 128, 2, 2, false),
-    BST_INST(AB_BF16, 256, 128, 2, 2, false),
-    BST_INST(AB_BF16, 128, 256, 2, 2, false),
-    BST_INST(AB_BF16, 128, 192, 2, 2, false),
-    BST_INST(AB_BF16, 128, 128, 2, 2, true),
-    BST_INST(AB_I8, 64, 64, 2, 2, false),
-    BST_INST(AB_I8, 128, 128, 2, 2, false),
-    BST_INST(AB_I8, 256, 128, 2, 2, false),
-    BST_INST(AB_I8, 256, 256, 2, 2, false),
-    BST_INST(AB_I8, 64, 64, 2, 2, true),
-    BST_INST(AB_I8, 128, 128, 2, 2, true),
-    BST_INST(AB_I8, 256, 128, 2, 2, true),
-    BST_INST(AB_I8, 256, 256, 2, 2, true),
-    BST_INST(AB_E4M3, 64, 64, 2, 2, false),
-    BST_INST(AB_E4M3, 128, 128, 2, 2, false),
-    BST_INST(AB_E4M3, 256, 128, 2, 2, false),
-    BST_INST(AB_E4M3, 256, 256, 2, 2, false),
-};
-
 int kernel_ab(bst_dtype ab) { return ab == BST_MXE4M3 ? AB_E4M3 : (int)ab; }
 
-const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped) {
-  for (const Instance& in : kInstances)
-    if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
-        in.grouped == grouped)
-      return &in;
+const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped, bool dma) {
+  const InstanceList lists[] = {instances_f16(), instances_bf16(), instances_i8(),
+                                instances_fp8()};
+  for (const InstanceList& l : lists)
+    for (int i = 0; i < l.count; ++i) {
+      const Instance& in = l.begin[i];
+      if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
+          in.grouped == grouped && in.dma == dma)
+        return &in;
+    }
   return nullptr;
 }
 
@@ -176,8 +129,25 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Resolves the schedule.  kind 0: plain / batched (count = batch), kind 1:
 // grouped (count = G, M = total_m).  Validates the schedule fields and the
 // sizes that bound the task count; pointer checks are the callers'.
+// Layout facts that decide whether the LDS-DMA family can run a call.
+struct Layout {
+  int64_t lda = 0, ldb = 0;
+  const void* sa = nullptr;
+  const void* sb = nullptr;
+};
+
+bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, const Layout& L) {
+  const int64_t es = (int64_t)elem_size(ab), ce = 16 / es;
+  if (K % ce != 0 || N % ce != 0) return false;       // no 16-byte chunk straddles K or N
+  if ((int64_t)bm * L.lda * es >= (1LL << 31)) return false;  // 31-bit panel offsets
+  if ((int64_t)bk * L.ldb * es >= (1LL << 31)) return false;
+  if (ab == BST_MXE4M3 && (K % 128 != 0 || ((uintptr_t)L.sa & 3u) || ((uintptr_t)L.sb & 3u)))
+    return false;
+  return true;
+}
+
 bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
-                     const bst_sched* s, bool need_device, Plan& p) {
+                     const bst_sched* s, bool need_device, Plan& p, const Layout* L = nullptr) {
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (count < 0 || M < 0 || N < 0 || K < 0)
     return fail(BST_E_INVAL, "negative size (count %lld M %lld N %lld K %lld)", (long long)count,
@@ -204,10 +174,19 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
     d.tile_m = 128;
     d.tile_n = 128;
   }
-  p.inst = find_instance(ab, d.tile_m, d.tile_n, kind == 1);
-  if (!p.inst)
+  if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
+  const Instance* reg = find_instance(ab, d.tile_m, d.tile_n, kind == 1, false);
+  const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, kind == 1, true);
+  if (!reg && !dma)
     return fail(BST_E_UNSUPPORTED, "no %s kernel for dtype %d with tile %ux%u",
                 kind == 1 ? "grouped" : "plain", (int)ab, d.tile_m, d.tile_n);
+  const Layout lay = L ? *L : Layout{K, N, nullptr, nullptr};
+  const bool fits = dma && dma_fits(ab, N, K, d.tile_m, (uint32_t)dma->bk, lay);
+  if (d.path == 2 && !fits)
+    return fail(BST_E_UNSUPPORTED, "the LDS-DMA kernels need K and N in whole 16-byte chunks "
+                "(and K %% 128 == 0 for MX); use path 0 or 1");
+  p.inst = (d.path == 1 || !fits) ? reg : dma;
+  if (!p.inst) return fail(BST_E_UNSUPPORTED, "no kernel of the requested family for this tile");
   if (d.tile_k != 0 && d.tile_k != (uint32_t)p.inst->bk)
     return fail(BST_E_UNSUPPORTED, "tile_k %u: this dtype runs tile_k %d", d.tile_k,
                 p.inst->bk);
@@ -310,7 +289,8 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
                  (batch > 1 && (!stride_ok(strideA, es) || !stride_ok(strideB, es))))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
-  st = make_plan(0, ab, batch, M, N, K, s, true, p);
+  const Layout lay{lda, ldb, sa, sb};
+  st = make_plan(0, ab, batch, M, N, K, s, true, p, &lay);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
@@ -403,7 +383,8 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
                  !stride_ok(strideB, es))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
-  st = make_plan(1, ab, G, total_m, N, K, s, true, p);
+  const Layout lay{lda, ldb, nullptr, nullptr};
+  st = make_plan(1, ab, G, total_m, N, K, s, true, p, &lay);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
@@ -509,6 +490,7 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
   out->split_k = p.split;
   out->xcd_remap = p.remap;
   out->grid = p.grid;
+  out->path = p.inst->dma ? 2u : 1u;
   return BST_OK;
 }
 

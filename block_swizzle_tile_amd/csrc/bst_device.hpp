@@ -83,7 +83,7 @@ struct TileCoord {
   uint32_t m, n;
 };
 
-__device__ __forceinline__ TileCoord block_coord(uint32_t loopsM, uint32_t loopsN, uint32_t off,
+__host__ __device__ __forceinline__ TileCoord block_coord(uint32_t loopsM, uint32_t loopsN, uint32_t off,
                                                  uint32_t dir, uint32_t inner) {
   TileCoord c;
   if (dir == 0) {  // Zn
@@ -131,26 +131,29 @@ struct GroupTable {
   int64_t first_row[kMaxGroups + 1];
 };
 
+__host__ __device__ inline void fill_group_table(GroupTable& gt, const int32_t* group_m, int G,
+                                                 int64_t total_m, uint32_t BM, uint32_t loopsN) {
+  uint32_t t = 0;
+  int64_t r = 0;
+  for (int g = 0; g < G; ++g) {
+    gt.first_task[g] = t;
+    gt.first_row[g] = r;
+    int64_t mg = group_m[g] > 0 ? group_m[g] : 0;
+    if (mg > total_m - r) mg = total_m - r;
+    t += ((uint32_t)mg + BM - 1) / BM * loopsN;
+    r += mg;
+  }
+  gt.first_task[G] = t;
+  gt.first_row[G] = r;
+}
+
 __device__ __forceinline__ void build_group_table(GroupTable& gt, const GemmArgs& a, uint32_t BM,
                                                   uint32_t loopsN) {
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    int64_t r = 0;
-    for (int g = 0; g < a.G; ++g) {
-      gt.first_task[g] = t;
-      gt.first_row[g] = r;
-      int64_t mg = a.group_m[g] > 0 ? a.group_m[g] : 0;
-      if (mg > a.total_m - r) mg = a.total_m - r;
-      t += ((uint32_t)mg + BM - 1) / BM * loopsN;
-      r += mg;
-    }
-    gt.first_task[a.G] = t;
-    gt.first_row[a.G] = r;
-  }
+  if (threadIdx.x == 0) fill_group_table(gt, a.group_m, a.G, a.total_m, BM, loopsN);
   __syncthreads();
 }
 
-__device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t t, uint32_t BM, uint32_t BN,
+__host__ __device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t t, uint32_t BM, uint32_t BN,
                                             const GroupTable* gt) {
   Task k;
   const uint32_t loopsN = (a.N + BN - 1) / BN;
@@ -251,7 +254,7 @@ __device__ __forceinline__ void mfma32(Acc& acc, const Frag& bt, const Frag& at,
 }
 
 // XOR permutation of the eight 16-byte chunks of LDS row r.
-__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
+__host__ __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
 
 __device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
@@ -282,6 +285,156 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
 }
 
 // ---------------------------------------------------------------- kernel --
+// ------------------------------------------------------------ epilogue --
+// Shared by both kernel families: the fixed-order split-K fix-up and the
+// conversion / dequant / masked store of a wave's 32x32 sub-tiles.
+template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+struct Epilogue {
+  using T = Traits<AB>;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  using Acc = typename std::conditional<T::IS_INT, i32x16_t, f32x16_t>::type;
+
+  // Split-K: every slice stores its partial tile; the last slice to arrive
+  // adds the partials in slice order 0..split-1 (so the result does not
+  // depend on arrival order) and returns true; the others return false.  The
+  // tile's counter is back at zero when the last slice leaves.
+  __device__ __attribute__((always_inline)) static bool fixup(const GemmArgs& a,
+                                                              Acc (&acc)[FM][FN], uint32_t s,
+                                                              uint32_t t) {
+    if (a.split <= 1) return true;
+    __shared__ uint32_t last_flag;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = threadIdx.x & 63u;
+    const size_t tile_elems = (size_t)BM * BN;
+    // partial layout: [slice][tile][wave][sub-tile][lane][16 values]
+    const size_t lane_off = ((size_t)(wave * FM * FN) * 64 + lane) * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float* p = a.ws_part + ((size_t)s * a.tile_cap + t) * tile_elems + lane_off +
+                   (size_t)(i * FN + j) * 64 * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // copy the element out first: a bit_cast of a vector-element
+            // expression would read element 0
+            const auto x = acc[i][j][4 * q + e];
+            v[e] = __builtin_bit_cast(float, x);
+          }
+          *reinterpret_cast<f32x4_t*>(p + 4 * q) = v;
+        }
+      }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = atomicAdd(&a.ws_count[t], 1u);
+      last_flag = (prev == a.split - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (last_flag == 0) return false;
+    __threadfence();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        Acc sum;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum[e] = 0;
+        for (uint32_t ss = 0; ss < a.split; ++ss) {
+          const float* p = a.ws_part + ((size_t)ss * a.tile_cap + t) * tile_elems + lane_off +
+                           (size_t)(i * FN + j) * 64 * 16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = v[e];
+              if constexpr (T::IS_INT)
+                sum[4 * q + e] += __builtin_bit_cast(int, x);
+              else
+                sum[4 * q + e] += x;
+            }
+          }
+        }
+        acc[i][j] = sum;
+      }
+    if (threadIdx.x == 0) a.ws_count[t] = 0u;
+    return true;
+  }
+
+  // Output of one 32x32 sub-tile: lane holds rows l32, columns 8g + 4*hi + {0..3}.
+  __device__ __attribute__((always_inline)) static void store_out(const GemmArgs& a, const Task& tk, const Acc& v, int i, int j,
+                                   uint32_t wm, uint32_t wn) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t l32 = lane & 31u, hi = lane >> 5;
+    const uint32_t ml = wm * TM + i * 32 + l32;
+    if (ml >= tk.rows_valid) return;
+    const int64_t grow = tk.row0 + ml;
+    const bool deq = a.row_scale != nullptr;
+    const float rs = deq ? a.row_scale[grow] : 1.0f;
+    uint8_t* crow = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + grow * a.ldc) *
+                             (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;
+      if (nl >= tk.nAct) continue;
+      const uint32_t gn = tk.n * BN + nl;
+      float f[4];
+      int32_t iv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (T::IS_INT) {
+          iv[r] = v[4 * g + r];
+          f[r] = (float)iv[r];
+        } else {
+          f[r] = v[4 * g + r];
+          iv[r] = 0;
+        }
+      }
+      if (deq) {
+        const float* cs = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + gn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float c = (nl + r < tk.nAct) ? cs[r] : 0.0f;
+          f[r] = (f[r] * rs) * c;
+        }
+      }
+      const bool full = nl + 4 <= tk.nAct;
+      if (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16) {
+        uint16_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          h[r] = a.cdtype == OUT_F16 ? f32_to_f16_rne(f[r]) : f32_to_bf16_rne(f[r]);
+        uint16_t* p = reinterpret_cast<uint16_t*>(crow) + gn;
+        if (full) {
+          *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        } else {
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = h[r];
+        }
+      } else if (a.cdtype == OUT_F32) {
+        float* p = reinterpret_cast<float*>(crow) + gn;
+        if (full) *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
+        else
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = f[r];
+      } else {  // OUT_I32
+        int32_t* p = reinterpret_cast<int32_t*>(crow) + gn;
+        if (full) *reinterpret_cast<i32x4_t*>(p) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+        else
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < tk.nAct) p[r] = iv[r];
+      }
+    }
+  }
+
+};
+
 template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
 struct GemmKernel {
   using T = Traits<AB>;
@@ -302,6 +455,7 @@ struct GemmKernel {
   static constexpr int LDS_BYTES = 2 * (STAGE_BYTES + SCALE_BYTES);
   using Acc = typename std::conditional<T::IS_INT, i32x16_t, f32x16_t>::type;
   using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
+  using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(T::BK * T::ES == kRowBytes, "one stage = one 128-byte row");
@@ -319,35 +473,67 @@ struct GemmKernel {
                                     const uint8_t* Bb, const Task& tk, uint32_t kb0,
                                     uint32_t kend, const uint8_t* sab, const uint8_t* sbb) {
     const uint32_t tid = threadIdx.x;
+    const bool k_full = kb0 + T::BK <= kend;
+    // Interior stages (the common case) issue every 16-byte load back to
+    // back with no predicate; only stages that touch a tail take the masked
+    // path.  Both conditions are uniform across the workgroup.
+    if (k_full && tk.rows_valid == (uint32_t)BM) {
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const uint32_t q = tid + i * NT;
-      st.a[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (A_CHUNKS % NT == 0 || q < (uint32_t)A_CHUNKS) {
-        const uint32_t r = q >> 3, c = q & 7u;
-        const uint32_t gk = kb0 + c * CE;
-        if (r < tk.rows_valid && gk < kend) {
-          const int valid = (int)((kend - gk) < (uint32_t)CE ? (kend - gk) : CE) * T::ES;
-          st.a[i] = load16(Ab + ((int64_t)r * a.lda + gk) * T::ES, valid);
+      for (int i = 0; i < A_PER_T; ++i) {
+        const uint32_t q = tid + i * NT;
+        if (A_CHUNKS % NT == 0 || q < (uint32_t)A_CHUNKS) {
+          const uint32_t r = q >> 3, c = q & 7u;
+          st.a[i] = *reinterpret_cast<const u32x4_t*>(Ab + ((int64_t)r * a.lda + kb0 + c * CE) * T::ES);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const uint32_t q = tid + i * NT;
+        st.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (A_CHUNKS % NT == 0 || q < (uint32_t)A_CHUNKS) {
+          const uint32_t r = q >> 3, c = q & 7u;
+          const uint32_t gk = kb0 + c * CE;
+          if (r < tk.rows_valid && gk < kend) {
+            const int valid = (int)((kend - gk) < (uint32_t)CE ? (kend - gk) : CE) * T::ES;
+            st.a[i] = load16(Ab + ((int64_t)r * a.lda + gk) * T::ES, valid);
+          }
         }
       }
     }
+    if (k_full && tk.n * BN + BN <= a.N) {
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-      const uint32_t q = tid + i * NT;
-      const uint32_t kb_lo = q & ((1u << KB_LO) - 1u);
-      const uint32_t rest = q >> KB_LO;
-      const uint32_t nb = rest % NBC;
-      const uint32_t kb = (rest / NBC) * (1u << KB_LO) + kb_lo;
-      const uint32_t ncol = tk.n * BN + nb * CE;
-      const bool live = (B_BLOCKS % NT == 0 || q < (uint32_t)B_BLOCKS);
-      const int nvalid = ncol < a.N ? (int)((a.N - ncol) < (uint32_t)CE ? (a.N - ncol) : CE) * T::ES : 0;
+      for (int i = 0; i < B_PER_T; ++i) {
+        const uint32_t q = tid + i * NT;
+        if (!(B_BLOCKS % NT == 0 || q < (uint32_t)B_BLOCKS)) continue;
+        const uint32_t kb_lo = q & ((1u << KB_LO) - 1u);
+        const uint32_t rest = q >> KB_LO;
+        const uint32_t nb = rest % NBC;
+        const uint32_t kb = (rest / NBC) * (1u << KB_LO) + kb_lo;
+        const uint8_t* p = Bb + ((int64_t)(kb0 + kb * T::KBR) * a.ldb + tk.n * BN + nb * CE) * T::ES;
 #pragma unroll
-      for (int j = 0; j < T::KBR; ++j) {
-        const uint32_t gk = kb0 + kb * T::KBR + j;
-        st.b[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-        if (live && gk < kend && nvalid > 0)
-          st.b[i][j] = load16(Bb + ((int64_t)gk * a.ldb + ncol) * T::ES, nvalid);
+        for (int j = 0; j < T::KBR; ++j)
+          st.b[i][j] = *reinterpret_cast<const u32x4_t*>(p + (int64_t)j * a.ldb * T::ES);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) {
+        const uint32_t q = tid + i * NT;
+        const uint32_t kb_lo = q & ((1u << KB_LO) - 1u);
+        const uint32_t rest = q >> KB_LO;
+        const uint32_t nb = rest % NBC;
+        const uint32_t kb = (rest / NBC) * (1u << KB_LO) + kb_lo;
+        const uint32_t ncol = tk.n * BN + nb * CE;
+        const bool live = (B_BLOCKS % NT == 0 || q < (uint32_t)B_BLOCKS);
+        const int nvalid =
+            ncol < a.N ? (int)((a.N - ncol) < (uint32_t)CE ? (a.N - ncol) : CE) * T::ES : 0;
+#pragma unroll
+        for (int j = 0; j < T::KBR; ++j) {
+          const uint32_t gk = kb0 + kb * T::KBR + j;
+          st.b[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+          if (live && gk < kend && nvalid > 0)
+            st.b[i][j] = load16(Bb + ((int64_t)gk * a.ldb + ncol) * T::ES, nvalid);
+        }
       }
     }
     if constexpr (T::SCALED) {
@@ -490,76 +676,8 @@ struct GemmKernel {
     }
   }
 
-  // Output of one 32x32 sub-tile: lane holds rows l32, columns 8g + 4*hi + {0..3}.
-  __device__ static void store_out(const GemmArgs& a, const Task& tk, const Acc& v, int i, int j,
-                                   uint32_t wm, uint32_t wn) {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t l32 = lane & 31u, hi = lane >> 5;
-    const uint32_t ml = wm * TM + i * 32 + l32;
-    if (ml >= tk.rows_valid) return;
-    const int64_t grow = tk.row0 + ml;
-    const bool deq = a.row_scale != nullptr;
-    const float rs = deq ? a.row_scale[grow] : 1.0f;
-    uint8_t* crow = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + grow * a.ldc) *
-                             (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16 ? 2 : 4);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;
-      if (nl >= tk.nAct) continue;
-      const uint32_t gn = tk.n * BN + nl;
-      float f[4];
-      int32_t iv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (T::IS_INT) {
-          iv[r] = v[4 * g + r];
-          f[r] = (float)iv[r];
-        } else {
-          f[r] = v[4 * g + r];
-          iv[r] = 0;
-        }
-      }
-      if (deq) {
-        const float* cs = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + gn;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float c = (nl + r < tk.nAct) ? cs[r] : 0.0f;
-          f[r] = (f[r] * rs) * c;
-        }
-      }
-      const bool full = nl + 4 <= tk.nAct;
-      if (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16) {
-        uint16_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = a.cdtype == OUT_F16 ? f32_to_f16_rne(f[r]) : f32_to_bf16_rne(f[r]);
-        uint16_t* p = reinterpret_cast<uint16_t*>(crow) + gn;
-        if (full) {
-          *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-        } else {
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = h[r];
-        }
-      } else if (a.cdtype == OUT_F32) {
-        float* p = reinterpret_cast<float*>(crow) + gn;
-        if (full) *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
-        else
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = f[r];
-      } else {  // OUT_I32
-        int32_t* p = reinterpret_cast<int32_t*>(crow) + gn;
-        if (full) *reinterpret_cast<i32x4_t*>(p) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
-        else
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = iv[r];
-      }
-    }
-  }
-
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    __shared__ uint32_t last_flag;
     GroupTable* gt = nullptr;
     uint32_t T_tiles = a.tiles;
     if constexpr (GROUPED) {
@@ -612,72 +730,11 @@ struct GemmKernel {
         }
       }
 
-      if (a.split > 1) {
-        // Fixed-order fix-up: every slice stores its partial tile; the last
-        // slice to arrive adds the partials in slice order 0..split-1 and
-        // writes the output.  The counter returns to zero for the next call.
-        const size_t tile_elems = (size_t)BM * BN;
-        const size_t lane_off = ((size_t)(wave * FM * FN) * 64 + lane) * 16;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            float* p = a.ws_part + ((size_t)s * a.tile_cap + t) * tile_elems + lane_off +
-                       (size_t)(i * FN + j) * 64 * 16;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              f32x4_t v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                // copy the element out first: a bit_cast of a vector-element
-                // expression would read element 0
-                const auto x = acc[i][j][4 * q + e];
-                v[e] = __builtin_bit_cast(float, x);
-              }
-              *reinterpret_cast<f32x4_t*>(p + 4 * q) = v;
-            }
-          }
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          const uint32_t prev = atomicAdd(&a.ws_count[t], 1u);
-          last_flag = (prev == a.split - 1) ? 1u : 0u;
-        }
-        __syncthreads();
-        if (last_flag == 0) continue;
-        __threadfence();
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            Acc sum;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sum[e] = 0;
-            for (uint32_t ss = 0; ss < a.split; ++ss) {
-              const float* p = a.ws_part + ((size_t)ss * a.tile_cap + t) * tile_elems + lane_off +
-                               (size_t)(i * FN + j) * 64 * 16;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + 4 * q);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float x = v[e];
-                  if constexpr (T::IS_INT)
-                    sum[4 * q + e] += __builtin_bit_cast(int, x);
-                  else
-                    sum[4 * q + e] += x;
-                }
-              }
-            }
-            acc[i][j] = sum;
-          }
-        if (threadIdx.x == 0) a.ws_count[t] = 0u;
-      }
-
+      if (!Epi::fixup(a, acc, s, t)) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) store_out(a, tk, acc[i][j], i, j, wm, wn);
+        for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
     }
   }
 };

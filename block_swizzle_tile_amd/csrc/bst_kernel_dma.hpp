@@ -1,0 +1,433 @@
+// bst_kernel_dma.hpp -- the fast kernel family: a multi-stage LDS-DMA
+// pipeline for gfx950.
+//
+// Every stage of A (BM x BK, K-contiguous rows of 128 bytes) and of B
+// (BK x BN, kept in its natural N-contiguous layout) is copied from global
+// memory straight into LDS with 16-byte `buffer_load ... lds` instructions:
+// no registers are spent on staging, so STAGES-1 stages can be in flight
+// while the MFMAs work on the oldest one (the buffering that "Block Dispatch
+// Policies" describes as ping-pong / preload between global memory and the
+// on-chip buffers, with the capacity rule stages x tile bytes <= LDS).
+// Out-of-range lanes of a buffer load write zeros, which masks every tail
+// (rows past the problem or group, K past the slice, columns past N) without
+// a branch.  Each lane picks the global 16-byte chunk that lands on its LDS
+// slot through an XOR permutation of the chunk index by the row, so the
+// MFMA operand reads below spread over the banks.
+//
+// Operand fetch per 32x32 MFMA: A with ds_read_b128 from the K-contiguous
+// rows; B^T with the gfx950 transposing reads ds_read_b64_tr_b16 /
+// ds_read_b64_tr_b8, each of which turns a 16-lane group's row-major 4 x 16
+// (16-bit) or 8 x 16 (8-bit) patch of B into one K-run of 4 / 8 values per
+// lane (lane layout established by an on-device probe).
+//
+// The MFMA, tail-shape, scheduler and epilogue code is shared with the
+// register-staged kernel of bst_device.hpp, which remains the path for
+// shapes whose K or N do not fill whole 16-byte chunks.
+#pragma once
+
+#include "bst_device.hpp"
+
+namespace bst {
+
+typedef __attribute__((address_space(3))) uint8_t lds_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+
+constexpr uint32_t kOob = 0x80000000u;  // a voffset that fails the buffer range check
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
+
+// One LDS array per pipeline stage, so that the compiler's wait-count pass
+// sees each stage as a separate object and only waits for the DMA into the
+// stage about to be read.
+template <int S, int BYTES>
+__device__ __forceinline__ lds_t* stage_buf() {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[BYTES];
+  return (lds_t*)buf;
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding), plus lgkmcnt(0) so that this wave's
+// LDS reads of older stages are complete before the barrier that follows.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)kOob,
+                                           kRsrcWord3);
+}
+
+// Largest power of two (at most 16) dividing n: the size of the aligned
+// chunk blocks inside which a B row is permuted.
+constexpr int pow2_block(int n) { return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1; }
+
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+struct DmaKernel {
+  using T = Traits<AB>;
+  using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
+  using Acc = typename Epi::Acc;
+  using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  static constexpr int ES = T::ES, BK = T::BK, CE = 16 / ES;
+  static constexpr int KSTEPS = BK / T::MFMA_K;
+  static constexpr int RB = BN * ES;     // bytes of one B row (one K index) in LDS
+  static constexpr int NCH = RB / 16;    // 16-byte chunks per B row
+  static constexpr uint32_t BSWZ = pow2_block(NCH) - 1;
+  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int B_BYTES = BK * RB;
+  static constexpr int A_IPW = A_BYTES / 1024 / NW;  // 1 KiB DMA instructions per wave
+  static constexpr int B_IPW = B_BYTES / 1024 / NW;
+  // MX scales: A as [rows][4 bytes] (one dword = the stage's 4 K blocks of a
+  // row), B as [4][BN] bytes; dword DMA, 256 bytes per instruction, padded so
+  // that every wave issues the same number of instructions.
+  static constexpr int SA_ROWS = T::SCALED ? (BM > 64 * NW ? BM : 64 * NW) : 0;
+  static constexpr int SA_BYTES = SA_ROWS * 4;
+  static constexpr int SB_BYTES = T::SCALED ? (4 * BN > 256 * NW ? 4 * BN : 256 * NW) : 0;
+  static constexpr int SA_IPW = SA_BYTES / 256 / NW;
+  static constexpr int SB_IPW = SB_BYTES / 256 / NW;
+  static constexpr int LPS = A_IPW + B_IPW + SA_IPW + SB_IPW;  // DMA instructions / wave / stage
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  static constexpr int WAIT_N = LPS * (STAGES > 2 ? STAGES - 2 : 0);
+
+  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA waves");
+  static_assert(SA_BYTES % (256 * NW) == 0 && SB_BYTES % (256 * NW) == 0, "whole scale waves");
+  static_assert(WAIT_N < 64, "vmcnt holds 6 bits");
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 MFMA sub-tiles");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024 - (GROUPED ? (int)sizeof(GroupTable) : 0) - 16,
+                "LDS budget");
+
+  static __host__ __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
+    if constexpr (ES == 2)
+      return (((k & 1u) * 10u) + (((k >> 1) & 1u) * 4u)) & BSWZ;
+    else
+      return ((k & 7u) + (k & 1u) * 8u) & BSWZ;
+  }
+
+  // Per-task, per-lane DMA addressing (offsets inside the tile panels).
+  struct Lanes {
+    uint32_t a_off[A_IPW];   // byte offset of the chunk in the A panel (row, chunk)
+    uint32_t a_kc[A_IPW];    // K index of the chunk's first element inside the stage
+    uint32_t a_ok;           // bit i: the chunk's row is inside the problem / group
+    uint32_t b_off[B_IPW];   // byte offset inside one stage of the B panel
+    uint32_t b_k[B_IPW];     // K row inside the stage
+    uint32_t b_ok;           // bit i: the chunk's columns are inside N
+    uint32_t sa_off[SA_IPW > 0 ? SA_IPW : 1];
+    uint32_t sa_ok;
+    uint32_t sb_off[SB_IPW > 0 ? SB_IPW : 1];
+    uint32_t sb_ok;
+  };
+
+  struct Ctx {
+    const uint8_t* a_tile;   // A panel of the task (first row, K = 0)
+    const uint8_t* b_tile;   // B panel of the task (K = 0, first column)
+    const uint8_t* sa_tile;  // MX: first scale of the task's first row
+    const uint8_t* sb_tile;  // MX: first scale column of the task
+    int64_t ldb_bytes, ldsb;
+    uint32_t kend;
+    uint32_t wave;
+    uint32_t scaled;         // fp8 with block scales (else every scale is 2^0)
+    Lanes ln;
+  };
+
+  // One DMA lane access: enabled, and its byte offset from the panel base of
+  // the stage (A: a_tile + kb0*ES, B: b_tile + kb0*ldb*ES, scales: the
+  // stage's first scale).  A disabled access gets an offset that fails the
+  // buffer range check, so the lane writes zeros.
+  struct Access {
+    bool ok;
+    uint32_t voff;
+  };
+
+  // Per-task, per-lane addressing.  Host-callable so that a CPU check can
+  // run exactly this code over every lane, wave, stage and task.
+  __host__ __device__ static void lane_setup(Lanes& ln, uint32_t wave, uint32_t lane,
+                                             uint32_t rows_valid, uint32_t n_tile, uint32_t N,
+                                             int64_t lda, int64_t ldb_bytes, int64_t ldsa,
+                                             int64_t ldsb) {
+    ln.a_ok = 0;
+    for (int i = 0; i < A_IPW; ++i) {
+      const uint32_t r = (wave * A_IPW + i) * 8 + (lane >> 3);
+      const uint32_t ch = (lane & 7u) ^ swz(r);
+      ln.a_off[i] = (uint32_t)((int64_t)r * lda * ES) + ch * 16;
+      ln.a_kc[i] = ch * CE;
+      if (r < rows_valid) ln.a_ok |= 1u << i;
+    }
+    ln.b_ok = 0;
+    for (int i = 0; i < B_IPW; ++i) {
+      const uint32_t byte = (wave * B_IPW + i) * 1024 + lane * 16;
+      const uint32_t k = byte / RB;
+      const uint32_t ch = ((byte % RB) / 16) ^ swz_b(k);
+      ln.b_off[i] = (uint32_t)((int64_t)k * ldb_bytes) + ch * 16;
+      ln.b_k[i] = k;
+      if (n_tile * BN + ch * CE < N) ln.b_ok |= 1u << i;
+    }
+    ln.sa_ok = 0;
+    ln.sb_ok = 0;
+    if constexpr (T::SCALED) {
+      for (int i = 0; i < SA_IPW; ++i) {
+        const uint32_t r = (wave * SA_IPW + i) * 64 + lane;
+        ln.sa_off[i] = (uint32_t)((int64_t)r * ldsa);
+        if (r < (uint32_t)BM && r < rows_valid) ln.sa_ok |= 1u << i;
+      }
+      for (int i = 0; i < SB_IPW; ++i) {
+        const uint32_t byte = (wave * SB_IPW + i) * 256 + lane * 4;
+        const uint32_t e = byte / BN, col = byte % BN;
+        ln.sb_off[i] = (uint32_t)((int64_t)e * ldsb) + col;
+        if (e < 4 && n_tile * BN + col < N) ln.sb_ok |= 1u << i;
+      }
+    }
+  }
+
+  __host__ __device__ static Access a_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+    const bool kfull = kb0 + BK <= kend;
+    const bool ok = ((ln.a_ok >> i) & 1u) && (kfull || kb0 + ln.a_kc[i] < kend);
+    return Access{ok, ok ? ln.a_off[i] : kOob};
+  }
+  __host__ __device__ static Access b_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+    const bool kfull = kb0 + BK <= kend;
+    const bool ok = ((ln.b_ok >> i) & 1u) && (kfull || kb0 + ln.b_k[i] < kend);
+    return Access{ok, ok ? ln.b_off[i] : kOob};
+  }
+  // Scales: this family runs MX only with K a multiple of the stage depth,
+  // so all 4 blocks of a stage exist.
+  __host__ __device__ static Access sa_access(const Lanes& ln, int i) {
+    const bool ok = (ln.sa_ok >> i) & 1u;
+    return Access{ok, ok ? ln.sa_off[i] : kOob};
+  }
+  __host__ __device__ static Access sb_access(const Lanes& ln, int i) {
+    const bool ok = (ln.sb_ok >> i) & 1u;
+    return Access{ok, ok ? ln.sb_off[i] : kOob};
+  }
+  // LDS byte offsets, inside a stage, of DMA instruction i of a wave.
+  __host__ __device__ static uint32_t a_lds(uint32_t wave, int i) { return (wave * A_IPW + i) * 1024; }
+  __host__ __device__ static uint32_t b_lds(uint32_t wave, int i) {
+    return A_BYTES + (wave * B_IPW + i) * 1024;
+  }
+  __host__ __device__ static uint32_t sa_lds(uint32_t wave, int i) {
+    return A_BYTES + B_BYTES + (wave * SA_IPW + i) * 256;
+  }
+  __host__ __device__ static uint32_t sb_lds(uint32_t wave, int i) {
+    return A_BYTES + B_BYTES + SA_BYTES + (wave * SB_IPW + i) * 256;
+  }
+
+  // Enqueue the DMA of the stage starting at K index kb0 into stage buffer S.
+  template <int S>
+  __device__ static __forceinline__ void issue(const Ctx& c, uint32_t kb0) {
+    lds_t* base = stage_buf<S, STAGE_BYTES>();
+    const __amdgpu_buffer_rsrc_t ra = rsrc(c.a_tile + (int64_t)kb0 * ES);
+#pragma unroll
+    for (int i = 0; i < A_IPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + a_lds(c.wave, i)), 16,
+                                               a_access(c.ln, i, kb0, c.kend).voff, 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(c.b_tile + (int64_t)kb0 * c.ldb_bytes);
+#pragma unroll
+    for (int i = 0; i < B_IPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + b_lds(c.wave, i)), 16,
+                                               b_access(c.ln, i, kb0, c.kend).voff, 0, 0, 0);
+    if constexpr (T::SCALED) {
+      if (c.scaled) {
+        const __amdgpu_buffer_rsrc_t rsa = rsrc(c.sa_tile + kb0 / 32);
+#pragma unroll
+        for (int i = 0; i < SA_IPW; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t*)(base + sa_lds(c.wave, i)), 4,
+                                                   sa_access(c.ln, i).voff, 0, 0, 0);
+        const __amdgpu_buffer_rsrc_t rsb = rsrc(c.sb_tile + (int64_t)(kb0 / 32) * c.ldsb);
+#pragma unroll
+        for (int i = 0; i < SB_IPW; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(base + sb_lds(c.wave, i)), 4,
+                                                   sb_access(c.ln, i).voff, 0, 0, 0);
+      }
+    }
+  }
+
+  // MFMAs over the stage held in buffer S.
+  template <int S>
+  __device__ static __forceinline__ void compute(Acc (&acc)[FM][FN], uint32_t wm, uint32_t wn,
+                                                 uint32_t scaled) {
+    const lds_t* base = stage_buf<S, STAGE_BYTES>();
+    const lds_t* la = base;
+    const lds_t* lb = base + A_BYTES;
+    const lds_t* lsa = base + A_BYTES + B_BYTES;
+    const lds_t* lsb = lsa + SA_BYTES;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t l32 = lane & 31u, hi = lane >> 5;
+    const uint32_t L = lane & 15u, half_group = (lane >> 4) & 1u;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      Frag fa[FM], fb[FN];
+      uint32_t sca[FM], scb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t row = wm * TM + i * 32 + l32;
+        const lds_t* rp = la + row * kRowBytes;
+        if constexpr (T::FRAG_DW == 4) {
+          fa[i] = *(const lds_u32x4_t*)(rp + (((2 * kk + hi) ^ swz(row)) << 4));
+        } else {
+          const u32x4_t x = *(const lds_u32x4_t*)(rp + (((4 * kk + hi) ^ swz(row)) << 4));
+          const u32x4_t y = *(const lds_u32x4_t*)(rp + (((4 * kk + 2 + hi) ^ swz(row)) << 4));
+          fa[i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+        }
+        if constexpr (T::SCALED)
+          sca[i] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * kk + hi))) & 0xffu
+                          : 0x7fu;
+        else
+          sca[i] = 0;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t cbase = wn * TN + j * 32 + 16 * half_group;  // first column of the group
+        if constexpr (ES == 2) {
+          // two transposing reads: K rows 16kk + 8hi + {0..3} and {4..7}
+          const uint32_t colb = (cbase + 4 * (L & 3u)) * 2;
+          i16x4_t v[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint32_t k = 16 * kk + 8 * hi + 4 * t + (L >> 2);
+            const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
+            v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+          }
+          fb[j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4,
+                                                                      5, 6, 7));
+        } else {
+          const uint32_t colb = cbase + 8 * (L & 1u);
+          constexpr int NR = T::FRAG_DW / 2;  // 8-byte transposing reads per operand
+          i32x2_t v[NR];
+#pragma unroll
+          for (int t = 0; t < NR; ++t) {
+            // int8: K rows 32kk + 16hi + 8t + {0..7}; fp8: the two 16-byte
+            // pieces of a lane come from the two halves of the 64-wide step
+            const uint32_t k = (NR == 2) ? 32 * kk + 16 * hi + 8 * t + (L >> 1)
+                                         : 64 * kk + 32 * (t >> 1) + 16 * hi + 8 * (t & 1) + (L >> 1);
+            const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
+            v[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
+          }
+          if constexpr (NR == 2)
+            fb[j] = u32x4_t{(uint32_t)v[0][0], (uint32_t)v[0][1], (uint32_t)v[1][0],
+                            (uint32_t)v[1][1]};
+          else
+            fb[j] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+        }
+        if constexpr (T::SCALED)
+          scb[j] = scaled ? lsb[(2 * kk + hi) * BN + wn * TN + j * 32 + l32] : 0x7fu;
+        else
+          scb[j] = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma32<AB>(acc[i][j], fb[j], fa[i], scb[j], sca[i]);
+    }
+  }
+
+  // One K step of the pipeline; stage kt lives in buffer S = kt % STAGES.
+  template <int S>
+  __device__ static __forceinline__ void step(Acc (&acc)[FM][FN], const Ctx& c, uint32_t k0,
+                                              uint32_t kt, uint32_t nk, uint32_t wm,
+                                              uint32_t wn) {
+    if (kt >= nk) return;
+    if (kt + STAGES - 2 < nk)
+      wait_vm_lgkm0<WAIT_N>();
+    else
+      wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue<(S + STAGES - 1) % STAGES>(c, k0 + (kt + STAGES - 1) * BK);
+    compute<S>(acc, wm, wn, c.scaled);
+  }
+
+  __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
+    GroupTable* gt = nullptr;
+    uint32_t T_tiles = a.tiles;
+    if constexpr (GROUPED) {
+      __shared__ GroupTable gtab;
+      gt = &gtab;
+      build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
+      T_tiles = gtab.first_task[a.G];
+    }
+    const uint32_t units = T_tiles * a.split;
+    Ctx c;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.ldb_bytes = a.ldb * ES;
+    c.ldsb = a.ldsb;
+    const uint32_t wm = c.wave / WN, wn = c.wave % WN;
+
+    for (uint32_t u = logical_wg(a.remap); u < units; u += gridDim.x) {
+      const uint32_t s = u / T_tiles;
+      const uint32_t t = u - s * T_tiles;
+      Task tk = decode_task(a, t, BM, BN, gt);
+      if constexpr (GROUPED) {
+        // the group table lives in LDS: make the task wave-uniform so that
+        // the buffer descriptors below stay in scalar registers
+        tk.idx = __builtin_amdgcn_readfirstlane(tk.idx);
+        tk.m = __builtin_amdgcn_readfirstlane(tk.m);
+        tk.n = __builtin_amdgcn_readfirstlane(tk.n);
+        tk.mAct = __builtin_amdgcn_readfirstlane(tk.mAct);
+        tk.nAct = __builtin_amdgcn_readfirstlane(tk.nAct);
+        tk.rows_valid = __builtin_amdgcn_readfirstlane(tk.rows_valid);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)tk.row0);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tk.row0 >> 32));
+        tk.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
+      }
+      const uint32_t k0 = s * a.kslice;
+      const uint32_t k1 = (k0 >= a.K || a.K - k0 < a.kslice) ? a.K : k0 + a.kslice;
+      const uint32_t nk = k0 < k1 ? (k1 - k0 + BK - 1) / BK : 0u;
+      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      c.a_tile = a.A + (bidx * a.strideA + tk.row0 * a.lda) * ES;
+      c.b_tile = a.B + ((int64_t)tk.idx * a.strideB + (int64_t)tk.n * BN) * ES;
+      c.scaled = (T::SCALED && a.sa != nullptr && a.sb != nullptr) ? 1u : 0u;
+      c.sa_tile = c.scaled ? a.sa + tk.row0 * a.ldsa : nullptr;
+      c.sb_tile = c.scaled ? a.sb + (int64_t)tk.n * BN : nullptr;
+      c.kend = k1;
+      lane_setup(c.ln, c.wave, threadIdx.x & 63u, tk.rows_valid, tk.n, a.N, a.lda, c.ldb_bytes,
+                 a.ldsa, a.ldsb);
+
+      Acc acc[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+      if (nk > 0) {
+        issue<0>(c, k0);
+        if (STAGES > 2 && 1 < nk) issue<1 % STAGES>(c, k0 + BK);
+        if (STAGES > 3 && 2 < nk) issue<2 % STAGES>(c, k0 + 2 * BK);
+        for (uint32_t kt = 0; kt < nk; kt += STAGES) {
+          step<0>(acc, c, k0, kt, nk, wm, wn);
+          step<1 % STAGES>(acc, c, k0, kt + 1, nk, wm, wn);
+          if constexpr (STAGES > 2) step<2 % STAGES>(acc, c, k0, kt + 2, nk, wm, wn);
+          if constexpr (STAGES > 3) step<3 % STAGES>(acc, c, k0, kt + 3, nk, wm, wn);
+        }
+        // every wave is done with the stage buffers before the next task's
+        // prologue refills them
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+      }
+
+      if (!Epi::fixup(a, acc, s, t)) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
+    }
+  }
+};
+
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only builtins: device pass only
+  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>::run(a);
+#endif
+}
+
+}  // namespace bst

@@ -1,0 +1,19 @@
+// inst_i8.hip -- compiled kernel instances for int8 operands.
+#include "bst_instances.hpp"
+
+namespace bst {
+
+static const Instance kList[] = {
+    BST_REG(AB_I8, 64, 64, 2, 2, false),    BST_REG(AB_I8, 128, 128, 2, 2, false),
+    BST_REG(AB_I8, 256, 128, 2, 2, false),  BST_REG(AB_I8, 256, 256, 4, 2, false),
+    BST_REG(AB_I8, 64, 64, 2, 2, true),     BST_REG(AB_I8, 128, 128, 2, 2, true),
+    BST_REG(AB_I8, 256, 128, 2, 2, true),   BST_REG(AB_I8, 256, 256, 4, 2, true),
+    BST_DMA(AB_I8, 64, 64, 2, 2, 4, false),    BST_DMA(AB_I8, 128, 128, 2, 2, 4, false),
+    BST_DMA(AB_I8, 256, 128, 2, 2, 3, false),  BST_DMA(AB_I8, 256, 256, 4, 2, 2, false),
+    BST_DMA(AB_I8, 64, 64, 2, 2, 4, true),     BST_DMA(AB_I8, 128, 128, 2, 2, 4, true),
+    BST_DMA(AB_I8, 256, 128, 2, 2, 3, true),   BST_DMA(AB_I8, 256, 256, 4, 2, 2, true),
+};
+
+InstanceList instances_i8() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }
+
+}  // namespace bst

@@ -76,6 +76,9 @@ typedef struct bst_sched {
                                   renumbered so that each XCD (accelerator die, own L2)
                                   takes a contiguous range of task indices */
   uint32_t grid;               /* persistent workgroups; 0 = fill every CU */
+  uint32_t path;               /* kernel family: 0 = automatic, 1 = register-staged (any shape),
+                                  2 = LDS-DMA pipeline (K and N whole 16-byte chunks, MX K a
+                                  multiple of 128; BST_E_UNSUPPORTED otherwise) */
 } bst_sched;
 
 /*

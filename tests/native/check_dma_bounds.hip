@@ -1,0 +1,295 @@
+// Host-side bounds and coverage check of the LDS-DMA kernels' addressing.
+//
+// Runs, on the CPU, the same addressing code the GPU kernels run
+// (DmaKernel::lane_setup / a_access / b_access / sa_access / sb_access and
+// the LDS offset helpers, plus the scheduler's decode_task and
+// fill_group_table) over every task, K slice, pipeline stage, wave and lane
+// of many problems, and checks that
+//   1. every enabled global access (16 bytes of A or B, 4 bytes of a scale
+//      block) lies inside the valid rows and columns of its matrix;
+//   2. every LDS destination lies inside the stage buffer;
+//   3. each stage loads every valid chunk of the tile exactly once.
+// Prints "ALL OK" and exits 0, or prints the first violation and exits 1.
+// Build: hipcc --cuda-host-only -std=c++17 -I include -I <csrc> check_dma_bounds.hip
+#include <cstdio>
+#include <cstdlib>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "bst_kernel_dma.hpp"
+
+using namespace bst;
+
+static int g_fail = 0;
+static long long g_checked = 0;
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) {                                  \
+      if (g_fail < 10) {                            \
+        printf("VIOLATION %s:%d: ", __FILE__, __LINE__); \
+        printf(__VA_ARGS__);                        \
+        printf("\n");                               \
+      }                                             \
+      ++g_fail;                                     \
+    }                                               \
+  } while (0)
+
+struct Problem {
+  std::string name;
+  int64_t batch = 1, M = 0, N = 0, K = 0, lda = 0, ldb = 0, strideA = 0, strideB = 0;
+  std::vector<int32_t> groups;  // non-empty: grouped (M = total_m)
+  uint32_t split = 1;
+  bool scaled = false;
+};
+
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+void check(const Problem& p) {
+  using KN = DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>;
+  constexpr int ES = KN::ES, BK = KN::BK, CE = KN::CE, NW = KN::NW;
+  // schedule: the same split resolution as the host planner (no empty slices)
+  const int64_t nk_all = (p.K + BK - 1) / BK;
+  int64_t split = p.split;
+  if (nk_all == 0) split = 1;
+  const int64_t ks_steps = nk_all > 0 ? (nk_all + split - 1) / split : 0;
+  if (ks_steps > 0) split = (nk_all + ks_steps - 1) / ks_steps;
+  const uint32_t kslice = (uint32_t)(ks_steps * BK);
+
+  GemmArgs a{};
+  a.M = (uint32_t)p.M;
+  a.N = (uint32_t)p.N;
+  a.K = (uint32_t)p.K;
+  a.off = 2;
+  a.dir = 0;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldsa = p.K / 32;
+  a.ldsb = p.N;
+  a.total_m = p.M;
+  GroupTable gt;
+  const GroupTable* gtp = nullptr;
+  const uint32_t loopsN = (uint32_t)((p.N + BN - 1) / BN);
+  uint32_t T;
+  if (GROUPED) {
+    a.G = (int)p.groups.size();
+    fill_group_table(gt, p.groups.data(), a.G, p.M, BM, loopsN);
+    gtp = &gt;
+    T = gt.first_task[a.G];
+  } else {
+    T = (uint32_t)(p.batch * ((p.M + BM - 1) / BM) * loopsN);
+  }
+  const int64_t rowbytesA = p.lda * ES, rowbytesB = p.ldb * ES;
+  for (uint32_t s = 0; s < split; ++s) {
+    for (uint32_t t = 0; t < T; ++t) {
+      const Task tk = decode_task(a, t, BM, BN, gtp);
+      const uint32_t k0 = s * kslice;
+      const uint32_t k1 = (k0 >= a.K || a.K - k0 < kslice) ? a.K : k0 + kslice;
+      const uint32_t nk = k0 < k1 ? (k1 - k0 + BK - 1) / BK : 0u;
+      // valid rows of the tile in the stacked A (group or batch problem)
+      int64_t row_lo = tk.row0, row_hi = tk.row0 + tk.rows_valid;
+      int64_t prob_rows;  // rows of this problem / group, for the bound check
+      int64_t prob_first;
+      if (GROUPED) {
+        prob_first = gt.first_row[tk.idx];
+        prob_rows = gt.first_row[tk.idx + 1] - prob_first;
+      } else {
+        prob_first = 0;
+        prob_rows = p.M;
+      }
+      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      const int64_t a_tile = (bidx * p.strideA + tk.row0 * p.lda) * ES;  // bytes from A
+      const int64_t b_tile = ((int64_t)tk.idx * p.strideB + (int64_t)tk.n * BN) * ES;
+      for (uint32_t kt = 0; kt < nk; ++kt) {
+        const uint32_t kb0 = k0 + kt * BK;
+        std::vector<int> covA(BM * 8, 0), covB(BK * KN::NCH, 0);
+        std::vector<int> covSA(BM, 0), covSB(4 * BN, 0);
+        for (uint32_t w = 0; w < (uint32_t)NW; ++w) {
+          for (uint32_t lane = 0; lane < 64; ++lane) {
+            typename KN::Lanes ln;
+            KN::lane_setup(ln, w, lane, tk.rows_valid, tk.n, a.N, a.lda, rowbytesB, a.ldsa,
+                           a.ldsb);
+            for (int i = 0; i < KN::A_IPW; ++i) {
+              const uint32_t lds = KN::a_lds(w, i) + lane * 16;
+              REQUIRE(lds + 16 <= (uint32_t)KN::A_BYTES, "A lds %u", lds);
+              const auto x = KN::a_access(ln, i, kb0, k1);
+              ++g_checked;
+              if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled A lane in range"); continue; }
+              REQUIRE(x.voff < kOob, "A voff %u", x.voff);
+              const int64_t addr = a_tile + (int64_t)kb0 * ES + x.voff;  // from batch base
+              const int64_t rel = addr - bidx * p.strideA * ES;
+              const int64_t R = rel / rowbytesA, cb = rel % rowbytesA;
+              REQUIRE(R >= row_lo && R < row_hi && R >= prob_first &&
+                          R < prob_first + prob_rows,
+                      "%s A row %lld outside [%lld,%lld)", p.name.c_str(), (long long)R,
+                      (long long)row_lo, (long long)row_hi);
+              REQUIRE(cb + 16 <= p.K * ES && cb >= (int64_t)kb0 * ES && cb < (int64_t)k1 * ES,
+                      "%s A col byte %lld (K %lld, kb0 %u, kend %u)", p.name.c_str(),
+                      (long long)cb, (long long)p.K, kb0, k1);
+              // coverage: which (row, chunk) of the tile stage landed where
+              const int64_t r = R - tk.row0, c = (cb - (int64_t)kb0 * ES) / 16;
+              if (r >= 0 && r < BM && c >= 0 && c < 8) {
+                covA[r * 8 + c]++;
+                REQUIRE((lds / 128) == (uint32_t)r && ((lds % 128) / 16) == (c ^ swz(r)),
+                        "A chunk (%lld,%lld) at lds %u", (long long)r, (long long)c, lds);
+              }
+            }
+            for (int i = 0; i < KN::B_IPW; ++i) {
+              const uint32_t lds = KN::b_lds(w, i) + lane * 16;
+              REQUIRE(lds + 16 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES), "B lds %u", lds);
+              const auto x = KN::b_access(ln, i, kb0, k1);
+              ++g_checked;
+              if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled B lane in range"); continue; }
+              REQUIRE(x.voff < kOob, "B voff %u", x.voff);
+              const int64_t rel = b_tile - (int64_t)tk.idx * p.strideB * ES +
+                                  (int64_t)kb0 * rowbytesB + x.voff;
+              const int64_t R = rel / rowbytesB, cb = rel % rowbytesB;
+              REQUIRE(R >= kb0 && R < k1 && R < p.K, "%s B row %lld (kb0 %u kend %u)",
+                      p.name.c_str(), (long long)R, kb0, k1);
+              REQUIRE(cb + 16 <= p.N * ES && cb >= (int64_t)tk.n * BN * ES &&
+                          cb < ((int64_t)tk.n * BN + BN) * ES,
+                      "%s B col byte %lld (N %lld)", p.name.c_str(), (long long)cb,
+                      (long long)p.N);
+              const int64_t k = R - kb0, c = (cb - (int64_t)tk.n * BN * ES) / 16;
+              covB[k * KN::NCH + c]++;
+              const uint32_t lb = lds - KN::A_BYTES;
+              REQUIRE(lb / KN::RB == (uint32_t)k && (lb % KN::RB) / 16 == (c ^ KN::swz_b(k)),
+                      "B chunk (%lld,%lld) at lds %u", (long long)k, (long long)c, lb);
+            }
+            if (KN::T::SCALED && p.scaled) {
+              for (int i = 0; i < KN::SA_IPW; ++i) {
+                const uint32_t lds = KN::sa_lds(w, i) + lane * 4;
+                REQUIRE(lds + 4 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES), "SA lds");
+                const auto x = KN::sa_access(ln, i);
+                ++g_checked;
+                if (!x.ok) continue;
+                const int64_t addr = tk.row0 * a.ldsa + kb0 / 32 + x.voff;
+                const int64_t R = addr / a.ldsa, c = addr % a.ldsa;
+                REQUIRE(R >= row_lo && R < row_hi && c + 4 <= a.ldsa && c == kb0 / 32,
+                        "%s SA row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
+                covSA[R - tk.row0]++;
+              }
+              for (int i = 0; i < KN::SB_IPW; ++i) {
+                const uint32_t lds = KN::sb_lds(w, i) + lane * 4;
+                REQUIRE(lds + 4 <= (uint32_t)KN::STAGE_BYTES, "SB lds");
+                const auto x = KN::sb_access(ln, i);
+                ++g_checked;
+                if (!x.ok) continue;
+                const int64_t addr = (int64_t)tk.n * BN + (int64_t)(kb0 / 32) * a.ldsb + x.voff;
+                const int64_t R = addr / a.ldsb, c = addr % a.ldsb;
+                REQUIRE(R >= kb0 / 32 && R < kb0 / 32 + 4 && R < p.K / 32 && c + 4 <= p.N,
+                        "%s SB row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
+                for (int e = 0; e < 4; ++e) covSB[(R - kb0 / 32) * BN + (c - tk.n * BN) + e]++;
+              }
+            }
+          }
+        }
+        // coverage: every valid chunk exactly once, nothing else
+        for (int r = 0; r < BM; ++r)
+          for (int c = 0; c < 8; ++c) {
+            const bool want = (uint32_t)r < tk.rows_valid && kb0 + c * CE < k1;
+            REQUIRE(covA[r * 8 + c] == (want ? 1 : 0), "%s A coverage r %d c %d = %d",
+                    p.name.c_str(), r, c, covA[r * 8 + c]);
+          }
+        for (int k = 0; k < BK; ++k)
+          for (int c = 0; c < KN::NCH; ++c) {
+            const bool want = kb0 + k < k1 && tk.n * BN + c * CE < a.N;
+            REQUIRE(covB[k * KN::NCH + c] == (want ? 1 : 0), "%s B coverage k %d c %d = %d",
+                    p.name.c_str(), k, c, covB[k * KN::NCH + c]);
+          }
+        if (KN::T::SCALED && p.scaled) {
+          for (int r = 0; r < BM; ++r)
+            REQUIRE(covSA[r] == ((uint32_t)r < tk.rows_valid ? 1 : 0), "SA coverage %d", r);
+          for (int e = 0; e < 4; ++e)
+            for (int c = 0; c < BN; ++c)
+              REQUIRE(covSB[e * BN + c] == (tk.n * BN + c < a.N ? 1 : 0), "SB coverage");
+        }
+      }
+    }
+  }
+}
+
+static Problem plain(const char* n, int64_t M, int64_t N, int64_t K, int64_t pad_a, int64_t pad_b,
+                     uint32_t split, int64_t batch = 1, bool scaled = false) {
+  Problem p;
+  p.name = n;
+  p.M = M; p.N = N; p.K = K;
+  p.lda = K + pad_a; p.ldb = N + pad_b;
+  p.batch = batch;
+  p.strideA = M * p.lda; p.strideB = K * p.ldb;
+  p.split = split;
+  p.scaled = scaled;
+  return p;
+}
+
+static Problem grouped(const char* n, std::vector<int32_t> g, int64_t spare, int64_t N, int64_t K,
+                       uint32_t split) {
+  Problem p;
+  p.name = n;
+  int64_t tot = 0;
+  for (int32_t x : g) tot += x > 0 ? x : 0;
+  p.M = tot + spare; p.N = N; p.K = K;
+  p.lda = K; p.ldb = N; p.strideB = K * N;
+  p.groups = g;
+  p.split = split;
+  return p;
+}
+
+template <int AB, int BM, int BN, int WM, int WN, int S>
+void run_plain(const std::vector<Problem>& ps) {
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, false>(p);
+}
+template <int AB, int BM, int BN, int WM, int WN, int S>
+void run_grouped(const std::vector<Problem>& ps) {
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, true>(p);
+}
+
+int main() {
+  // 16-bit operands: K and N multiples of 8 elements
+  const std::vector<Problem> p16 = {
+      plain("tails", 200, 136, 256, 0, 0, 1),      plain("tails-split", 200, 136, 256, 8, 16, 3),
+      plain("tiny", 1, 8, 8, 0, 0, 1),             plain("ragged", 129, 264, 1000, 24, 8, 2),
+      plain("2k", 1024, 1024, 2048, 0, 0, 4),      plain("kslice", 77, 8, 520, 8, 8, 5),
+      plain("flat", 300, 1000, 64, 0, 0, 1),       plain("batch", 100, 200, 136, 8, 0, 2, 3),
+      plain("k0", 33, 40, 0, 8, 0, 1)};
+  const std::vector<Problem> g16 = {grouped("g16", {0, 1, 300, 0, 127, 129, 5}, 9, 136, 264, 1),
+                                    grouped("g16s", {64, 0, 200}, 0, 128, 512, 3)};
+  run_plain<AB_F16, 64, 64, 2, 2, 4>(p16);
+  run_plain<AB_F16, 128, 128, 2, 2, 4>(p16);
+  run_plain<AB_F16, 256, 128, 2, 2, 3>(p16);
+  run_plain<AB_F16, 128, 256, 2, 2, 3>(p16);
+  run_plain<AB_F16, 128, 192, 2, 2, 3>(p16);
+  run_grouped<AB_F16, 128, 128, 2, 2, 4>(g16);
+  // 8-bit operands: K and N multiples of 16
+  const std::vector<Problem> p8 = {
+      plain("tails8", 200, 144, 256, 0, 0, 1),   plain("t8split", 333, 528, 384, 16, 16, 3),
+      plain("tiny8", 1, 16, 16, 0, 0, 1),        plain("big8", 1024, 1024, 1024, 0, 0, 2),
+      plain("k8", 65, 32, 1040, 16, 0, 4),       plain("batch8", 50, 272, 256, 0, 16, 1, 2)};
+  const std::vector<Problem> g8 = {
+      grouped("g8", {0, 1, 300, 0, 0, 127, 129, 5, 0}, 9, 144, 96, 1),
+      grouped("g8s", {1562, 1426, 784, 1108, 234, 823, 101, 154}, 0, 512, 256, 2),
+      grouped("g8e", {0, 0}, 5, 64, 128, 1)};
+  run_plain<AB_I8, 64, 64, 2, 2, 4>(p8);
+  run_plain<AB_I8, 128, 128, 2, 2, 4>(p8);
+  run_plain<AB_I8, 256, 128, 2, 2, 3>(p8);
+  run_plain<AB_I8, 256, 256, 4, 2, 2>(p8);
+  run_grouped<AB_I8, 64, 64, 2, 2, 4>(g8);
+  run_grouped<AB_I8, 128, 128, 2, 2, 4>(g8);
+  run_grouped<AB_I8, 256, 128, 2, 2, 3>(g8);
+  run_grouped<AB_I8, 256, 256, 4, 2, 2>(g8);
+  // fp8: plain (no scales) and MX (K a multiple of 128)
+  std::vector<Problem> p8f = p8;
+  p8f.push_back(plain("mx", 256, 512, 1024, 0, 0, 1, 1, true));
+  p8f.push_back(plain("mxtail", 200, 144, 384, 128, 16, 2, 1, true));
+  p8f.push_back(plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true));
+  run_plain<AB_E4M3, 64, 64, 2, 2, 4>(p8f);
+  run_plain<AB_E4M3, 128, 128, 2, 2, 4>(p8f);
+  run_plain<AB_E4M3, 256, 128, 2, 2, 3>(p8f);
+  run_plain<AB_E4M3, 256, 256, 4, 2, 2>(p8f);
+  if (g_fail) {
+    printf("FAILED: %d violations (%lld accesses checked)\n", g_fail, g_checked);
+    return 1;
+  }
+  printf("ALL OK (%lld accesses checked)\n", g_checked);
+  return 0;
+}

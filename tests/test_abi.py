@@ -109,7 +109,15 @@ def test_effective_sched_split_resolution(L):
     s = S(tile=(128, 128), split_k=3)
     assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 2048, ctypes.byref(s),
                                  ctypes.byref(out)) == _lib.OK
-    assert out.split_k == 3 and out.grid >= 1
+    assert out.split_k == 3 and out.grid >= 1 and out.path == 2
+    # K not a whole number of 16-byte chunks: only the register-staged family
+    assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 60, ctypes.byref(S(tile=(64, 64))),
+                                 ctypes.byref(out)) == _lib.OK and out.path == 1
+    assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 60,
+                                 ctypes.byref(S(tile=(64, 64), path=2)),
+                                 ctypes.byref(out)) == _lib.E_UNSUPPORTED
+    assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 64, ctypes.byref(S(path=3)),
+                                 ctypes.byref(out)) == _lib.E_INVAL
 
 
 def test_grouped_validation(L):

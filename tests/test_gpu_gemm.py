@@ -55,7 +55,10 @@ def test_tails_workload_fp16(orc):
                   dict(tile=(128, 128), offset=2, direction="raster"),
                   dict(tile=(64, 64), offset=3, direction="zn", split_k=2),
                   dict(tile=(128, 192), offset=1, direction="zn", split_k=4, grid=5),
-                  dict(tile=(256, 128), offset=3, direction="nz", grid=1)]:
+                  dict(tile=(256, 128), offset=3, direction="nz", grid=1),
+                  dict(tile=(64, 64), offset=3, direction="zn", path=1),
+                  dict(tile=(64, 64), offset=3, direction="zn", path=2),
+                  dict(tile=(128, 128), offset=2, split_k=3, path=2, xcd_remap=1)]:
         say("tails", sched)
         C = bst().gemm(A, B, sched=bst().make_sched(**sched))
         check_close(orc, C, ref, den, TOL_16, str(sched))
@@ -114,7 +117,11 @@ def test_k_zero_and_empty(orc):
     dict(tile=(256, 128), offset=o, direction=d) for o in (1, 2, 4, 8) for d in ("zn", "nz")
 ] + [dict(tile=(128, 128), offset=2, split_k=4), dict(tile=(256, 128), offset=1, split_k=8,
                                                        xcd_remap=1),
-     dict(tile=(128, 128), offset=1, split_k=0, xcd_remap=1)])
+     dict(tile=(128, 128), offset=1, split_k=0, xcd_remap=1),
+     dict(tile=(128, 128), offset=2, split_k=4, path=1),
+     dict(tile=(256, 128), offset=4, direction="nz", path=1),
+     dict(tile=(128, 256), offset=2, split_k=2, path=2),
+     dict(tile=(64, 64), offset=8, path=2, xcd_remap=1)])
 def test_fp16_2k_workload(orc, fp16_2k, sched):
     """1024x1024x2048 fp16, every swizzle setting at 256x128 plus split-K forms."""
     w, ref, den = fp16_2k
@@ -134,7 +141,7 @@ def test_bf16_batch_workload(orc):
                         strideB=K * N, tile=w["tile"], rows=rows)
     A, B = to_gpu(w["A"], "bf16"), to_gpu(w["B"], "bf16")
     for sched in [dict(tile=(128, 192), offset=1), dict(tile=(256, 128), offset=2, direction="nz"),
-                  dict(tile=(128, 128), offset=4, xcd_remap=1)]:
+                  dict(tile=(128, 128), offset=4, xcd_remap=1), dict(tile=(128, 192), path=1)]:
         say("bf16 batch", sched)
         C = bst().batched_gemm(A, B, sched=bst().make_sched(**sched))
         check_close(orc, take(C.reshape(b * M, N), rows), ref, den, TOL_16, str(sched))
@@ -158,7 +165,9 @@ def test_mxfp8_small_full(orc):
     A, B = to_gpu(w["A"], "e4m3"), to_gpu(w["B"], "e4m3")
     sa, sb = to_gpu(w["scale_a"], "u8"), to_gpu(w["scale_b"], "u8")
     for sched in [dict(tile=(128, 128)), dict(tile=(256, 256), offset=4),
-                  dict(tile=(64, 64), offset=2, direction="nz", split_k=2)]:
+                  dict(tile=(64, 64), offset=2, direction="nz", split_k=2),
+                  dict(tile=(128, 128), path=1), dict(tile=(256, 128), path=1, split_k=2),
+                  dict(tile=(256, 128), path=2, offset=3), dict(tile=(64, 64), path=2)]:
         say("mxfp8 small", sched)
         C = bst().gemm(A, B, scale_a=sa, scale_b=sb, sched=bst().make_sched(**sched))
         check_close(orc, C, ref, den, TOL_8, str(sched))
@@ -197,7 +206,9 @@ def test_int8_groups_small_full(orc):
     gmt = to_gpu(gm, "i32")
     rs, cs = to_gpu(w["row_scale"], "f32"), to_gpu(w["col_scale"], "f32")
     for sched in [dict(tile=(64, 64)), dict(tile=(128, 128), offset=2, direction="nz"),
-                  dict(tile=(256, 256), offset=1, split_k=2), dict(tile=(256, 128), xcd_remap=1)]:
+                  dict(tile=(256, 256), offset=1, split_k=2), dict(tile=(256, 128), xcd_remap=1),
+                  dict(tile=(128, 128), path=1), dict(tile=(256, 256), path=1, offset=2),
+                  dict(tile=(64, 64), path=2, split_k=2), dict(tile=(256, 256), path=2)]:
         say("int8 groups small", sched)
         s = bst().make_sched(**sched)
         raw = bst().grouped_gemm_slice_m(A, B, gmt, sched=s)
@@ -268,7 +279,8 @@ def test_quant_gemm_per_token(orc):
     At, Bt = to_gpu(A, "i8"), to_gpu(B, "i8")
     rst, cst = to_gpu(rs, "f32"), to_gpu(cs.ravel(), "f32")
     import torch
-    for sched in [dict(tile=(128, 128)), dict(tile=(256, 256), split_k=3, offset=2)]:
+    for sched in [dict(tile=(128, 128)), dict(tile=(256, 256), split_k=3, offset=2),
+                  dict(tile=(128, 128), path=1), dict(tile=(256, 128), path=2, split_k=2)]:
         say("quant per token", sched)
         s = bst().make_sched(**sched)
         out = bst().quant_gemm_per_token(At, Bt, rst, cst, sched=s)
@@ -295,7 +307,8 @@ def test_determinism_and_split_invariance(orc):
     At, Bt = to_gpu(A, "i8"), to_gpu(B, "i8")
     base = codes(bst().gemm(At, Bt, sched=bst().make_sched(tile=(128, 128))))
     for s in [dict(tile=(64, 64), split_k=8), dict(tile=(256, 256), direction="nz", offset=3),
-              dict(tile=(256, 128), split_k=2, xcd_remap=1)]:
+              dict(tile=(256, 128), split_k=2, xcd_remap=1), dict(tile=(128, 128), path=1),
+              dict(tile=(128, 128), path=2), dict(tile=(256, 256), path=1, split_k=3)]:
         assert np.array_equal(codes(bst().gemm(At, Bt, sched=bst().make_sched(**s))), base)
     Ai = I.f16_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64))
     Bi = I.f16_bits(g.integers(-4, 5, size=(K, N)).astype(np.float64))
