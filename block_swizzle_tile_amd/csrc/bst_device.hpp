@@ -299,6 +299,18 @@ struct Epilogue {
   // adds the partials in slice order 0..split-1 (so the result does not
   // depend on arrival order) and returns true; the others return false.  The
   // tile's counter is back at zero when the last slice leaves.
+  //
+  // The slices of a tile may run on different XCDs, whose L2 caches are not
+  // coherent with each other.  Partials are therefore written and read with
+  // the device-scope cache policy (the L2 writes them through and never
+  // serves them stale) and ordered by waiting for the stores to complete
+  // before the arrival counter is bumped.  This avoids device-scope fences,
+  // which write back and invalidate the whole L2 and so cost every other
+  // workgroup on the XCD its cached A and B panels.  Partial tile layout:
+  // [wave][sub-tile][quarter][lane][4 values], so every wave instruction
+  // moves 1 KiB of contiguous memory.
+  static constexpr int kDeviceScope = 16;  // cache policy bit sc1 on gfx950
+
   __device__ __attribute__((always_inline)) static bool fixup(const GemmArgs& a,
                                                               Acc (&acc)[FM][FN], uint32_t s,
                                                               uint32_t t) {
@@ -306,37 +318,39 @@ struct Epilogue {
     __shared__ uint32_t last_flag;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = threadIdx.x & 63u;
-    const size_t tile_elems = (size_t)BM * BN;
-    // partial layout: [slice][tile][wave][sub-tile][lane][16 values]
-    const size_t lane_off = ((size_t)(wave * FM * FN) * 64 + lane) * 16;
+    const size_t tile_bytes = (size_t)BM * BN * 4;
+    const uint32_t wave_off = wave * FM * FN * 4096u + lane * 16u;
+    {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)s * a.tile_cap + t) * tile_bytes,
+          (short)0, (int)tile_bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        float* p = a.ws_part + ((size_t)s * a.tile_cap + t) * tile_elems + lane_off +
-                   (size_t)(i * FN + j) * 64 * 16;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4_t v;
+          for (int q = 0; q < 4; ++q) {
+            u32x4_t v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // copy the element out first: a bit_cast of a vector-element
-            // expression would read element 0
-            const auto x = acc[i][j][4 * q + e];
-            v[e] = __builtin_bit_cast(float, x);
+            for (int e = 0; e < 4; ++e) {
+              // copy the element out first: a bit_cast of a vector-element
+              // expression would read element 0
+              const auto x = acc[i][j][4 * q + e];
+              v[e] = __builtin_bit_cast(uint32_t, x);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, wave_off + (i * FN + j) * 4096u + q * 1024u,
+                                                   0, kDeviceScope);
           }
-          *reinterpret_cast<f32x4_t*>(p + 4 * q) = v;
-        }
-      }
-    __threadfence();
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-      const uint32_t prev = atomicAdd(&a.ws_count[t], 1u);
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&a.ws_count[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_flag = (prev == a.split - 1) ? 1u : 0u;
     }
     __syncthreads();
     if (last_flag == 0) return false;
-    __threadfence();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -345,24 +359,27 @@ struct Epilogue {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sum[e] = 0;
         for (uint32_t ss = 0; ss < a.split; ++ss) {
-          const float* p = a.ws_part + ((size_t)ss * a.tile_cap + t) * tile_elems + lane_off +
-                           (size_t)(i * FN + j) * 64 * 16;
+          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)ss * a.tile_cap + t) * tile_bytes,
+              (short)0, (int)tile_bytes, 0x00020000);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + 4 * q);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                r, wave_off + (i * FN + j) * 4096u + q * 1024u, 0, kDeviceScope);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x = v[e];
+              const uint32_t x = v[e];
               if constexpr (T::IS_INT)
                 sum[4 * q + e] += __builtin_bit_cast(int, x);
               else
-                sum[4 * q + e] += x;
+                sum[4 * q + e] += __builtin_bit_cast(float, x);
             }
           }
         }
         acc[i][j] = sum;
       }
-    if (threadIdx.x == 0) a.ws_count[t] = 0u;
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.ws_count[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
 

@@ -51,17 +51,35 @@ __device__ __forceinline__ lds_t* stage_buf() {
   return (lds_t*)buf;
 }
 
-// s_waitcnt vmcnt(N) (gfx9 encoding), plus lgkmcnt(0) so that this wave's
-// LDS reads of older stages are complete before the barrier that follows.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+// Buffer descriptor over [base, base + 2^31): raw (stride 0) 32-bit data.
+__device__ __forceinline__ u32x4_t make_desc(const uint8_t* base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, kOob, (uint32_t)kRsrcWord3};
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)kOob,
-                                           kRsrcWord3);
+// Global -> LDS copies: lane i writes bytes [lds + 16i, +16) (or [lds + 4i,
+// +4)) from base + voff.  Issued as inline assembly so that the compiler
+// does not insert its own conservative wait for these LDS writes before
+// every LDS read; the pipeline's explicit vmcnt waits and barriers order
+// them instead.
+__device__ __forceinline__ void dma16(const u32x4_t& desc, const lds_t* lds, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(desc)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const u32x4_t& desc, const lds_t* lds, uint32_t voff) {
+  asm volatile("buffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(desc)
+               : "memory");
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Largest power of two (at most 16) dividing n: the size of the aligned
@@ -95,12 +113,11 @@ struct DmaKernel {
   static constexpr int SB_IPW = SB_BYTES / 256 / NW;
   static constexpr int LPS = A_IPW + B_IPW + SA_IPW + SB_IPW;  // DMA instructions / wave / stage
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static constexpr int WAIT_N = LPS * (STAGES > 2 ? STAGES - 2 : 0);
 
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA waves");
   static_assert(SA_BYTES % (256 * NW) == 0 && SB_BYTES % (256 * NW) == 0, "whole scale waves");
-  static_assert(WAIT_N < 64, "vmcnt holds 6 bits");
+  static_assert(LPS * STAGES < 64, "vmcnt holds 6 bits");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 MFMA sub-tiles");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024 - (GROUPED ? (int)sizeof(GroupTable) : 0) - 16,
                 "LDS budget");
@@ -223,36 +240,38 @@ struct DmaKernel {
   template <int S>
   __device__ static __forceinline__ void issue(const Ctx& c, uint32_t kb0) {
     lds_t* base = stage_buf<S, STAGE_BYTES>();
-    const __amdgpu_buffer_rsrc_t ra = rsrc(c.a_tile + (int64_t)kb0 * ES);
+    const u32x4_t ra = make_desc(c.a_tile + (int64_t)kb0 * ES);
 #pragma unroll
     for (int i = 0; i < A_IPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + a_lds(c.wave, i)), 16,
-                                               a_access(c.ln, i, kb0, c.kend).voff, 0, 0, 0);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(c.b_tile + (int64_t)kb0 * c.ldb_bytes);
+      dma16(ra, base + a_lds(c.wave, i), a_access(c.ln, i, kb0, c.kend).voff);
+    const u32x4_t rb = make_desc(c.b_tile + (int64_t)kb0 * c.ldb_bytes);
 #pragma unroll
     for (int i = 0; i < B_IPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + b_lds(c.wave, i)), 16,
-                                               b_access(c.ln, i, kb0, c.kend).voff, 0, 0, 0);
+      dma16(rb, base + b_lds(c.wave, i), b_access(c.ln, i, kb0, c.kend).voff);
     if constexpr (T::SCALED) {
       if (c.scaled) {
-        const __amdgpu_buffer_rsrc_t rsa = rsrc(c.sa_tile + kb0 / 32);
+        const u32x4_t rsa = make_desc(c.sa_tile + kb0 / 32);
 #pragma unroll
-        for (int i = 0; i < SA_IPW; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t*)(base + sa_lds(c.wave, i)), 4,
-                                                   sa_access(c.ln, i).voff, 0, 0, 0);
-        const __amdgpu_buffer_rsrc_t rsb = rsrc(c.sb_tile + (int64_t)(kb0 / 32) * c.ldsb);
+        for (int i = 0; i < SA_IPW; ++i) dma4(rsa, base + sa_lds(c.wave, i), sa_access(c.ln, i).voff);
+        const u32x4_t rsb = make_desc(c.sb_tile + (int64_t)(kb0 / 32) * c.ldsb);
 #pragma unroll
-        for (int i = 0; i < SB_IPW; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(base + sb_lds(c.wave, i)), 4,
-                                                   sb_access(c.ln, i).voff, 0, 0, 0);
+        for (int i = 0; i < SB_IPW; ++i) dma4(rsb, base + sb_lds(c.wave, i), sb_access(c.ln, i).voff);
       }
     }
   }
 
-  // MFMAs over the stage held in buffer S.
+  // A wave's MFMA operands of one whole stage, held in registers.
+  struct Frags {
+    Frag a[KSTEPS][FM];
+    Frag b[KSTEPS][FN];
+    uint32_t sa[KSTEPS][FM];
+    uint32_t sb[KSTEPS][FN];
+  };
+
+  // LDS -> registers: every operand fragment of stage buffer S.
   template <int S>
-  __device__ static __forceinline__ void compute(Acc (&acc)[FM][FN], uint32_t wm, uint32_t wn,
-                                                 uint32_t scaled) {
+  __device__ static __forceinline__ void load_frags(Frags& f, uint32_t wm, uint32_t wn,
+                                                    uint32_t scaled) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
     const lds_t* lb = base + A_BYTES;
@@ -263,25 +282,23 @@ struct DmaKernel {
     const uint32_t L = lane & 15u, half_group = (lane >> 4) & 1u;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      Frag fa[FM], fb[FN];
-      uint32_t sca[FM], scb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t row = wm * TM + i * 32 + l32;
         const lds_t* rp = la + row * kRowBytes;
         if constexpr (T::FRAG_DW == 4) {
-          fa[i] = *(const lds_u32x4_t*)(rp + (((2 * kk + hi) ^ swz(row)) << 4));
+          f.a[kk][i] = *(const lds_u32x4_t*)(rp + (((2 * kk + hi) ^ swz(row)) << 4));
         } else {
           const u32x4_t x = *(const lds_u32x4_t*)(rp + (((4 * kk + hi) ^ swz(row)) << 4));
           const u32x4_t y = *(const lds_u32x4_t*)(rp + (((4 * kk + 2 + hi) ^ swz(row)) << 4));
-          fa[i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
-                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+          f.a[kk][i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                               (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         }
         if constexpr (T::SCALED)
-          sca[i] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * kk + hi))) & 0xffu
-                          : 0x7fu;
+          f.sa[kk][i] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * kk + hi))) & 0xffu
+                               : 0x7fu;
         else
-          sca[i] = 0;
+          f.sa[kk][i] = 0;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -296,8 +313,8 @@ struct DmaKernel {
             const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
             v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
           }
-          fb[j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4,
-                                                                      5, 6, 7));
+          f.b[kk][j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3,
+                                                                           4, 5, 6, 7));
         } else {
           const uint32_t colb = cbase + 8 * (L & 1u);
           constexpr int NR = T::FRAG_DW / 2;  // 8-byte transposing reads per operand
@@ -312,36 +329,68 @@ struct DmaKernel {
             v[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
           }
           if constexpr (NR == 2)
-            fb[j] = u32x4_t{(uint32_t)v[0][0], (uint32_t)v[0][1], (uint32_t)v[1][0],
-                            (uint32_t)v[1][1]};
+            f.b[kk][j] = u32x4_t{(uint32_t)v[0][0], (uint32_t)v[0][1], (uint32_t)v[1][0],
+                                 (uint32_t)v[1][1]};
           else
-            fb[j] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+            f.b[kk][j] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
         }
         if constexpr (T::SCALED)
-          scb[j] = scaled ? lsb[(2 * kk + hi) * BN + wn * TN + j * 32 + l32] : 0x7fu;
+          f.sb[kk][j] = scaled ? lsb[(2 * kk + hi) * BN + wn * TN + j * 32 + l32] : 0x7fu;
         else
-          scb[j] = 0;
+          f.sb[kk][j] = 0;
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma32<AB>(acc[i][j], fb[j], fa[i], scb[j], sca[i]);
     }
   }
 
-  // One K step of the pipeline; stage kt lives in buffer S = kt % STAGES.
-  template <int S>
-  __device__ static __forceinline__ void step(Acc (&acc)[FM][FN], const Ctx& c, uint32_t k0,
-                                              uint32_t kt, uint32_t nk, uint32_t wm,
-                                              uint32_t wn) {
+  __device__ static __forceinline__ void mfma_frags(Acc (&acc)[FM][FN], const Frags& f) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          mfma32<AB>(acc[i][j], f.b[kk][j], f.a[kk][i], f.sb[kk][j], f.sa[kk][i]);
+  }
+
+  template <int N>
+  __device__ static __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+
+  // One K step; I counts steps modulo the unroll: stage kt lives in buffer
+  // I % STAGES, its fragments in register set `cur`.  The step makes stage
+  // kt+1 resident (own DMA complete, then a barrier, which also tells that
+  // every wave is done with the buffer the next DMA overwrites), issues the
+  // DMA of stage kt+STAGES-1, reads stage kt+1's fragments into `nxt`, and
+  // runs stage kt's MFMAs from `cur` while those reads are in flight.
+  template <int I>
+  __device__ static __forceinline__ void step(Acc (&acc)[FM][FN], Frags& cur, Frags& nxt,
+                                              const Ctx& c, uint32_t k0, uint32_t kt, uint32_t nk,
+                                              uint32_t wm, uint32_t wn) {
+    constexpr int S = I % STAGES;
     if (kt >= nk) return;
-    if (kt + STAGES - 2 < nk)
-      wait_vm_lgkm0<WAIT_N>();
-    else
-      wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue<(S + STAGES - 1) % STAGES>(c, k0 + (kt + STAGES - 1) * BK);
-    compute<S>(acc, wm, wn, c.scaled);
+    if constexpr (STAGES == 2) {
+      // Two buffers leave no room to read ahead: wait for stage kt, then
+      // refill the other buffer while computing from this one.
+      wait_vm<0>();
+      barrier_lds();
+      if (kt + 1 < nk) issue<(S + 1) % STAGES>(c, k0 + (kt + 1) * BK);
+      load_frags<S>(cur, wm, wn, c.scaled);
+      mfma_frags(acc, cur);
+    } else {
+      // stages issued so far: up to kt + STAGES - 2
+      if (kt + 1 < nk) {
+        if (kt + STAGES - 2 < nk)
+          wait_vm<LPS * (STAGES - 3)>();
+        else
+          wait_vm<0>();
+      }
+      barrier_lds();
+      if (kt + STAGES - 1 < nk) issue<(S + STAGES - 1) % STAGES>(c, k0 + (kt + STAGES - 1) * BK);
+      if (kt + 1 < nk) load_frags<(S + 1) % STAGES>(nxt, wm, wn, c.scaled);
+      mfma_frags(acc, cur);
+    }
   }
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
@@ -402,16 +451,34 @@ struct DmaKernel {
         issue<0>(c, k0);
         if (STAGES > 2 && 1 < nk) issue<1 % STAGES>(c, k0 + BK);
         if (STAGES > 3 && 2 < nk) issue<2 % STAGES>(c, k0 + 2 * BK);
-        for (uint32_t kt = 0; kt < nk; kt += STAGES) {
-          step<0>(acc, c, k0, kt, nk, wm, wn);
-          step<1 % STAGES>(acc, c, k0, kt + 1, nk, wm, wn);
-          if constexpr (STAGES > 2) step<2 % STAGES>(acc, c, k0, kt + 2, nk, wm, wn);
-          if constexpr (STAGES > 3) step<3 % STAGES>(acc, c, k0, kt + 3, nk, wm, wn);
+        Frags f0, f1;
+        if constexpr (STAGES > 2) {
+          // stage 0 resident and in registers before the first step
+          if (nk - 1 >= (uint32_t)(STAGES - 2))
+            wait_vm<LPS * (STAGES - 2)>();
+          else
+            wait_vm<0>();
+          barrier_lds();
+          load_frags<0>(f0, wm, wn, c.scaled);
+        }
+        // unrolled so that buffer index and register set are compile-time
+        constexpr int UNR = (STAGES % 2 == 0) ? STAGES : 2 * STAGES;
+        for (uint32_t kt = 0; kt < nk; kt += UNR) {
+          step<0>(acc, f0, f1, c, k0, kt, nk, wm, wn);
+          step<1>(acc, f1, f0, c, k0, kt + 1, nk, wm, wn);
+          if constexpr (UNR > 2) {
+            step<2>(acc, f0, f1, c, k0, kt + 2, nk, wm, wn);
+            step<3>(acc, f1, f0, c, k0, kt + 3, nk, wm, wn);
+          }
+          if constexpr (UNR > 4) {
+            step<4>(acc, f0, f1, c, k0, kt + 4, nk, wm, wn);
+            step<5>(acc, f1, f0, c, k0, kt + 5, nk, wm, wn);
+          }
         }
         // every wave is done with the stage buffers before the next task's
         // prologue refills them
         __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
+        barrier_lds();
       }
 
       if (!Epi::fixup(a, acc, s, t)) continue;
