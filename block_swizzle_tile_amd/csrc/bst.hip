@@ -20,6 +20,10 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+#ifdef BST_TRACE
+uint64_t* g_trace = nullptr;  // device buffer for the K-loop cycle accounting
+#endif
+
 bst_status fail(bst_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -139,8 +143,11 @@ struct Layout {
 bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, const Layout& L) {
   const int64_t es = (int64_t)elem_size(ab), ce = 16 / es;
   if (K % ce != 0 || N % ce != 0) return false;       // no 16-byte chunk straddles K or N
-  if ((int64_t)bm * L.lda * es >= (1LL << 31)) return false;  // 31-bit panel offsets
-  if ((int64_t)bk * L.ldb * es >= (1LL << 31)) return false;
+  // 31-bit panel offsets: lane offset (row / K row inside a stage) plus the
+  // stage's scalar offset (K position) stay below 2^31
+  if ((int64_t)bm * L.lda * es + K * es >= (1LL << 31)) return false;
+  if ((K + bk) * L.ldb * es >= (1LL << 31)) return false;
+  if (ab == BST_MXE4M3 && (K / 32 + 4) * N >= (1LL << 31)) return false;  // B scales [K/32][N]
   if (ab == BST_MXE4M3 && (K % 128 != 0 || ((uintptr_t)L.sa & 3u) || ((uintptr_t)L.sb & 3u)))
     return false;
   return true;
@@ -296,6 +303,9 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   if (st != BST_OK) return st;
 
   GemmArgs a{};
+#ifdef BST_TRACE
+  a.trace = g_trace;
+#endif
   a.A = static_cast<const uint8_t*>(A);
   a.B = static_cast<const uint8_t*>(B);
   a.C = static_cast<uint8_t*>(C);
@@ -321,6 +331,10 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
 }  // namespace
 
 extern "C" {
+
+#ifdef BST_TRACE
+void bst_debug_set_trace(void* dev_buf) { g_trace = (uint64_t*)dev_buf; }
+#endif
 
 const char* bst_last_error(void) { return g_err; }
 
@@ -389,6 +403,9 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
   GemmArgs a{};
+#ifdef BST_TRACE
+  a.trace = g_trace;
+#endif
   a.A = static_cast<const uint8_t*>(A);
   a.B = static_cast<const uint8_t*>(B);
   a.C = static_cast<uint8_t*>(C);
@@ -420,6 +437,9 @@ bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const
     return fail(BST_E_INVAL, "%llu tasks do not fit max_tasks %lld",
                 (unsigned long long)p.tile_cap, (long long)max_tasks);
   GemmArgs a{};
+#ifdef BST_TRACE
+  a.trace = g_trace;
+#endif
   a.M = (uint32_t)M; a.N = (uint32_t)N;
   a.batch = (uint32_t)batch;
   a.tiles = (uint32_t)p.tile_cap;
@@ -449,6 +469,9 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
                 (unsigned long long)p.tile_cap);
   if (p.tile_cap == 0) return BST_OK;
   GemmArgs a{};
+#ifdef BST_TRACE
+  a.trace = g_trace;
+#endif
   a.N = (uint32_t)N;
   a.group_m = group_m;
   a.G = G;

@@ -72,6 +72,7 @@ struct GemmArgs {
   uint32_t* ws_count;                 // split > 1: one arrival counter per tile
   uint32_t tile_cap;                  // tiles the workspace was sized for
   uint32_t* map_out;                  // map-dump kernel only
+  uint64_t* trace;                    // BST_TRACE builds only: per-wave cycle counts of workgroup 0
 };
 
 // ------------------------------------------------------------ scheduler ---

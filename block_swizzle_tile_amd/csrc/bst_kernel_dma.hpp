@@ -25,6 +25,9 @@
 // shapes whose K or N do not fill whole 16-byte chunks.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "bst_device.hpp"
 
 namespace bst {
@@ -58,20 +61,41 @@ __device__ __forceinline__ u32x4_t make_desc(const uint8_t* base) {
 }
 
 // Global -> LDS copies: lane i writes bytes [lds + 16i, +16) (or [lds + 4i,
-// +4)) from base + voff.  Issued as inline assembly so that the compiler
-// does not insert its own conservative wait for these LDS writes before
-// every LDS read; the pipeline's explicit vmcnt waits and barriers order
-// them instead.
-__device__ __forceinline__ void dma16(const u32x4_t& desc, const lds_t* lds, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds"
+// +4)) from base + soff + voff; a lane whose voff fails the descriptor's
+// range check writes zeros.  Issued as inline assembly so that the
+// compiler does not insert its own conservative wait for these LDS writes
+// before every LDS read; the pipeline's explicit vmcnt waits and barriers
+// order them instead.
+// The descriptor and the scalar offset are wave-uniform by construction;
+// readfirstlane states it, so that they always live in scalar registers.
+//
+// The compiler does not look inside inline assembly for hazards, and it
+// often writes these scalar operands (readfirstlane, or a reload of a
+// spilled scalar through v_readlane) with a vector instruction right
+// before the asm; the hardware needs 5 wait states between a vector-ALU
+// write of an SGPR and a vector-memory instruction reading it, and 1
+// between a write of M0 and an LDS DMA.  The asm therefore starts with
+// s_nop 4 (5 wait states).
+__device__ __forceinline__ u32x4_t uniform(const u32x4_t& d) {
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(d[0]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(d[1]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(d[2]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(d[3])};
+}
+__device__ __forceinline__ void dma16(const u32x4_t& desc, const lds_t* lds, uint32_t voff,
+                                      uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(desc)
+               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(uniform(desc)),
+                 "s"((uint32_t)__builtin_amdgcn_readfirstlane(soff))
                : "memory");
 }
-__device__ __forceinline__ void dma4(const u32x4_t& desc, const lds_t* lds, uint32_t voff) {
-  asm volatile("buffer_load_dword %1, %2, 0 offen lds"
+__device__ __forceinline__ void dma4(const u32x4_t& desc, const lds_t* lds, uint32_t voff,
+                                     uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(desc)
+               : "{m0}"((uint32_t)(uintptr_t)lds), "v"(voff), "s"(uniform(desc)),
+                 "s"((uint32_t)__builtin_amdgcn_readfirstlane(soff))
                : "memory");
 }
 
@@ -81,6 +105,69 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// Compile-time loops: f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, B + Is>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for_range(F&& f) {
+  if constexpr (E > B) static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_range<0, N>(f);
+}
+
+// Cycle accounting of the K loop (BST_TRACE builds only; empty otherwise):
+// time in the wait + barrier at the top of each step, and in the step bodies.
+struct LoopTrace {
+#ifdef BST_TRACE
+  uint64_t wait = 0, body = 0, mark = 0, start = 0, prologue = 0;
+#endif
+  __device__ __forceinline__ void begin() {
+#ifdef BST_TRACE
+    start = mark = __builtin_amdgcn_s_memtime();
+#endif
+  }
+  __device__ __forceinline__ void top() {  // before the wait of a step
+#ifdef BST_TRACE
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    body += t - mark;
+    mark = t;
+#endif
+  }
+  __device__ __forceinline__ void released() {  // after the barrier of a step
+#ifdef BST_TRACE
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    wait += t - mark;
+    mark = t;
+#endif
+  }
+  __device__ __forceinline__ void prologue_done() {
+#ifdef BST_TRACE
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    prologue = t - start;
+    mark = t;
+#endif
+  }
+  __device__ __forceinline__ void finish(uint64_t* out) {
+#ifdef BST_TRACE
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    body += t - mark;
+    if (out != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
+      const uint32_t w = threadIdx.x >> 6;
+      out[w * 4 + 0] += wait;
+      out[w * 4 + 1] += body;
+      out[w * 4 + 2] += prologue;
+      out[w * 4 + 3] += t - start;
+    }
+#else
+    (void)out;
+#endif
+  }
+};
 
 // Largest power of two (at most 16) dividing n: the size of the aligned
 // chunk blocks inside which a B row is permuted.
@@ -149,6 +236,8 @@ struct DmaKernel {
     const uint8_t* sa_tile;  // MX: first scale of the task's first row
     const uint8_t* sb_tile;  // MX: first scale column of the task
     int64_t ldb_bytes, ldsb;
+    uint32_t ldb_bytes32, ldsb32;  // the same, known below 2^31 per panel
+    uint32_t k0;             // first K index of the task's slice
     uint32_t kend;
     uint32_t wave;
     uint32_t scaled;         // fp8 with block scales (else every scale is 2^0)
@@ -166,7 +255,7 @@ struct DmaKernel {
 
   // Per-task, per-lane addressing.  Host-callable so that a CPU check can
   // run exactly this code over every lane, wave, stage and task.
-  __host__ __device__ static void lane_setup(Lanes& ln, uint32_t wave, uint32_t lane,
+  __host__ __device__ __forceinline__ static void lane_setup(Lanes& ln, uint32_t wave, uint32_t lane,
                                              uint32_t rows_valid, uint32_t n_tile, uint32_t N,
                                              int64_t lda, int64_t ldb_bytes, int64_t ldsa,
                                              int64_t ldsb) {
@@ -204,152 +293,238 @@ struct DmaKernel {
     }
   }
 
-  __host__ __device__ static Access a_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+  __host__ __device__ __forceinline__ static Access a_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
     const bool kfull = kb0 + BK <= kend;
     const bool ok = ((ln.a_ok >> i) & 1u) && (kfull || kb0 + ln.a_kc[i] < kend);
     return Access{ok, ok ? ln.a_off[i] : kOob};
   }
-  __host__ __device__ static Access b_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+  __host__ __device__ __forceinline__ static Access b_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
     const bool kfull = kb0 + BK <= kend;
     const bool ok = ((ln.b_ok >> i) & 1u) && (kfull || kb0 + ln.b_k[i] < kend);
     return Access{ok, ok ? ln.b_off[i] : kOob};
   }
   // Scales: this family runs MX only with K a multiple of the stage depth,
-  // so all 4 blocks of a stage exist.
-  __host__ __device__ static Access sa_access(const Lanes& ln, int i) {
-    const bool ok = (ln.sa_ok >> i) & 1u;
+  // so a stage inside [0, kend) has all 4 blocks; a padding stage past kend
+  // reads none.
+  __host__ __device__ __forceinline__ static Access sa_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+    const bool ok = ((ln.sa_ok >> i) & 1u) && kb0 < kend;
     return Access{ok, ok ? ln.sa_off[i] : kOob};
   }
-  __host__ __device__ static Access sb_access(const Lanes& ln, int i) {
-    const bool ok = (ln.sb_ok >> i) & 1u;
+  __host__ __device__ __forceinline__ static Access sb_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+    const bool ok = ((ln.sb_ok >> i) & 1u) && kb0 < kend;
     return Access{ok, ok ? ln.sb_off[i] : kOob};
   }
   // LDS byte offsets, inside a stage, of DMA instruction i of a wave.
-  __host__ __device__ static uint32_t a_lds(uint32_t wave, int i) { return (wave * A_IPW + i) * 1024; }
-  __host__ __device__ static uint32_t b_lds(uint32_t wave, int i) {
+  __host__ __device__ __forceinline__ static uint32_t a_lds(uint32_t wave, int i) { return (wave * A_IPW + i) * 1024; }
+  __host__ __device__ __forceinline__ static uint32_t b_lds(uint32_t wave, int i) {
     return A_BYTES + (wave * B_IPW + i) * 1024;
   }
-  __host__ __device__ static uint32_t sa_lds(uint32_t wave, int i) {
+  __host__ __device__ __forceinline__ static uint32_t sa_lds(uint32_t wave, int i) {
     return A_BYTES + B_BYTES + (wave * SA_IPW + i) * 256;
   }
-  __host__ __device__ static uint32_t sb_lds(uint32_t wave, int i) {
+  __host__ __device__ __forceinline__ static uint32_t sb_lds(uint32_t wave, int i) {
     return A_BYTES + B_BYTES + SA_BYTES + (wave * SB_IPW + i) * 256;
   }
 
-  // Enqueue the DMA of the stage starting at K index kb0 into stage buffer S.
-  template <int S>
-  __device__ static __forceinline__ void issue(const Ctx& c, uint32_t kb0) {
-    lds_t* base = stage_buf<S, STAGE_BYTES>();
-    const u32x4_t ra = make_desc(c.a_tile + (int64_t)kb0 * ES);
-#pragma unroll
-    for (int i = 0; i < A_IPW; ++i)
-      dma16(ra, base + a_lds(c.wave, i), a_access(c.ln, i, kb0, c.kend).voff);
-    const u32x4_t rb = make_desc(c.b_tile + (int64_t)kb0 * c.ldb_bytes);
-#pragma unroll
-    for (int i = 0; i < B_IPW; ++i)
-      dma16(rb, base + b_lds(c.wave, i), b_access(c.ln, i, kb0, c.kend).voff);
+  // Per-task DMA state: buffer descriptors over the task's panels and, for
+  // a task whose every stage lies inside its K slice (no partial and no
+  // padding stage), each instruction's lane offset with the lane's row /
+  // column validity folded in (kOob outside).  The K position of a stage
+  // reaches the address through the instruction's scalar offset, so a
+  // steady-state DMA is an M0 write and the load.  Without block scales the
+  // scale slots still issue, with every lane out of range (they write
+  // zeros and read nothing), so that each stage is exactly LPS
+  // instructions for the vmcnt arithmetic.
+  struct Dma {
+    u32x4_t ra, rb, rsa, rsb;
+    uint32_t vo[LPS];
+  };
+
+  // Lane offset of DMA instruction X when the stage is entirely inside the
+  // slice (host-callable, so the CPU check compares it with the checked
+  // per-stage offsets).
+  __host__ __device__ __forceinline__ static uint32_t full_voff(const Lanes& ln, int X, bool scaled) {
+    if (X < A_IPW) return ((ln.a_ok >> X) & 1u) ? ln.a_off[X] : kOob;
+    if (X < A_IPW + B_IPW) {
+      const int i = X - A_IPW;
+      return ((ln.b_ok >> i) & 1u) ? ln.b_off[i] : kOob;
+    }
+    if (X < A_IPW + B_IPW + SA_IPW) {
+      const int i = X - A_IPW - B_IPW;
+      return (scaled && ((ln.sa_ok >> i) & 1u)) ? ln.sa_off[i] : kOob;
+    }
+    const int i = X - A_IPW - B_IPW - SA_IPW;
+    return (scaled && ((ln.sb_ok >> i) & 1u)) ? ln.sb_off[i] : kOob;
+  }
+
+  template <bool FULL>
+  __device__ static __forceinline__ Dma make_dma(const Ctx& c) {
+    Dma d;
+    d.ra = make_desc(c.a_tile);
+    d.rb = make_desc(c.b_tile);
     if constexpr (T::SCALED) {
-      if (c.scaled) {
-        const u32x4_t rsa = make_desc(c.sa_tile + kb0 / 32);
+      d.rsa = make_desc(c.scaled ? c.sa_tile : c.a_tile);
+      d.rsb = make_desc(c.scaled ? c.sb_tile : c.a_tile);
+    }
+    if constexpr (FULL) {
 #pragma unroll
-        for (int i = 0; i < SA_IPW; ++i) dma4(rsa, base + sa_lds(c.wave, i), sa_access(c.ln, i).voff);
-        const u32x4_t rsb = make_desc(c.sb_tile + (int64_t)(kb0 / 32) * c.ldsb);
-#pragma unroll
-        for (int i = 0; i < SB_IPW; ++i) dma4(rsb, base + sb_lds(c.wave, i), sb_access(c.ln, i).voff);
-      }
+      for (int x = 0; x < LPS; ++x) d.vo[x] = full_voff(c.ln, x, c.scaled != 0);
+    }
+    return d;
+  }
+
+  // Scalar byte offsets of the stage at K index kb0 inside each panel.
+  struct Soff {
+    uint32_t kb0, a, b, sa, sb;
+  };
+  __device__ static __forceinline__ Soff stage_soff(const Ctx& c, uint32_t kb0) {
+    return Soff{kb0, kb0 * (uint32_t)ES, kb0 * c.ldb_bytes32, kb0 / 32u, (kb0 / 32u) * c.ldsb32};
+  }
+
+  // DMA instruction X (0 <= X < LPS) of this wave for the stage of `so`,
+  // into stage buffer S.
+  template <int S, int X, bool FULL>
+  __device__ static __forceinline__ void dma_one(const Ctx& c, const Dma& d, const Soff& so) {
+    lds_t* base = stage_buf<S, STAGE_BYTES>();
+    if constexpr (X < A_IPW) {
+      const uint32_t v = FULL ? d.vo[X] : a_access(c.ln, X, so.kb0, c.kend).voff;
+      dma16(d.ra, base + a_lds(c.wave, X), v, so.a);
+    } else if constexpr (X < A_IPW + B_IPW) {
+      constexpr int i = X - A_IPW;
+      const uint32_t v = FULL ? d.vo[X] : b_access(c.ln, i, so.kb0, c.kend).voff;
+      dma16(d.rb, base + b_lds(c.wave, i), v, so.b);
+    } else if constexpr (X < A_IPW + B_IPW + SA_IPW) {
+      constexpr int i = X - A_IPW - B_IPW;
+      const uint32_t v =
+          FULL ? d.vo[X] : (c.scaled ? sa_access(c.ln, i, so.kb0, c.kend).voff : kOob);
+      dma4(d.rsa, base + sa_lds(c.wave, i), v, so.sa);
+    } else {
+      constexpr int i = X - A_IPW - B_IPW - SA_IPW;
+      const uint32_t v =
+          FULL ? d.vo[X] : (c.scaled ? sb_access(c.ln, i, so.kb0, c.kend).voff : kOob);
+      dma4(d.rsb, base + sb_lds(c.wave, i), v, so.sb);
     }
   }
 
-  // A wave's MFMA operands of one whole stage, held in registers.
-  struct Frags {
-    Frag a[KSTEPS][FM];
-    Frag b[KSTEPS][FN];
-    uint32_t sa[KSTEPS][FM];
-    uint32_t sb[KSTEPS][FN];
+  // Enqueue the whole DMA of the stage at K index kb0 into stage buffer S.
+  template <int S, bool FULL>
+  __device__ static __forceinline__ void issue(const Ctx& c, const Dma& d, uint32_t kb0) {
+    const Soff so = stage_soff(c, kb0);
+    static_for<LPS>([&](auto x) { dma_one<S, decltype(x)::value, FULL>(c, d, so); });
+  }
+
+  // MFMA operands of one K step of a wave, held in registers.
+  struct KFrag {
+    Frag a[FM];
+    Frag b[FN];
+    uint32_t sa[FM];
+    uint32_t sb[FN];
   };
 
-  // LDS -> registers: every operand fragment of stage buffer S.
-  template <int S>
-  __device__ static __forceinline__ void load_frags(Frags& f, uint32_t wm, uint32_t wn,
-                                                    uint32_t scaled) {
+  // LDS -> registers, one operand fragment at a time: A fragment I and B
+  // fragment J of K step KK of stage buffer S, with their block scales.
+  template <int S, int KK, int I>
+  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, uint32_t scaled) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
-    const lds_t* lb = base + A_BYTES;
     const lds_t* lsa = base + A_BYTES + B_BYTES;
-    const lds_t* lsb = lsa + SA_BYTES;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t l32 = lane & 31u, hi = lane >> 5;
+    const uint32_t row = wm * TM + I * 32 + l32;
+    const lds_t* rp = la + row * kRowBytes;
+    if constexpr (T::FRAG_DW == 4) {
+      f.a[I] = *(const lds_u32x4_t*)(rp + (((2 * KK + hi) ^ swz(row)) << 4));
+    } else {
+      const u32x4_t x = *(const lds_u32x4_t*)(rp + (((4 * KK + hi) ^ swz(row)) << 4));
+      const u32x4_t y = *(const lds_u32x4_t*)(rp + (((4 * KK + 2 + hi) ^ swz(row)) << 4));
+      f.a[I] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                       (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    }
+    if constexpr (T::SCALED)
+      f.sa[I] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * KK + hi))) & 0xffu : 0x7fu;
+    else
+      f.sa[I] = 0;
+  }
+
+  template <int S, int KK, int J>
+  __device__ static __forceinline__ void load_b(KFrag& f, uint32_t wn, uint32_t scaled) {
+    const lds_t* base = stage_buf<S, STAGE_BYTES>();
+    const lds_t* lb = base + A_BYTES;
+    const lds_t* lsb = base + A_BYTES + B_BYTES + SA_BYTES;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
     const uint32_t L = lane & 15u, half_group = (lane >> 4) & 1u;
+    const uint32_t cbase = wn * TN + J * 32 + 16 * half_group;  // first column of the group
+    if constexpr (ES == 2) {
+      // two transposing reads: K rows 16kk + 8hi + {0..3} and {4..7}
+      const uint32_t colb = (cbase + 4 * (L & 3u)) * 2;
+      i16x4_t v[2];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t row = wm * TM + i * 32 + l32;
-        const lds_t* rp = la + row * kRowBytes;
-        if constexpr (T::FRAG_DW == 4) {
-          f.a[kk][i] = *(const lds_u32x4_t*)(rp + (((2 * kk + hi) ^ swz(row)) << 4));
-        } else {
-          const u32x4_t x = *(const lds_u32x4_t*)(rp + (((4 * kk + hi) ^ swz(row)) << 4));
-          const u32x4_t y = *(const lds_u32x4_t*)(rp + (((4 * kk + 2 + hi) ^ swz(row)) << 4));
-          f.a[kk][i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
-                               (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-        }
-        if constexpr (T::SCALED)
-          f.sa[kk][i] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * kk + hi))) & 0xffu
-                               : 0x7fu;
-        else
-          f.sa[kk][i] = 0;
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t k = 16 * KK + 8 * hi + 4 * t + (L >> 2);
+        const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
+        v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
       }
+      f.b[J] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3,
+                                                                   4, 5, 6, 7));
+    } else {
+      const uint32_t colb = cbase + 8 * (L & 1u);
+      constexpr int NR = T::FRAG_DW / 2;  // 8-byte transposing reads per operand
+      i32x2_t v[NR];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t cbase = wn * TN + j * 32 + 16 * half_group;  // first column of the group
-        if constexpr (ES == 2) {
-          // two transposing reads: K rows 16kk + 8hi + {0..3} and {4..7}
-          const uint32_t colb = (cbase + 4 * (L & 3u)) * 2;
-          i16x4_t v[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint32_t k = 16 * kk + 8 * hi + 4 * t + (L >> 2);
-            const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
-            v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
-          }
-          f.b[kk][j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3,
-                                                                           4, 5, 6, 7));
-        } else {
-          const uint32_t colb = cbase + 8 * (L & 1u);
-          constexpr int NR = T::FRAG_DW / 2;  // 8-byte transposing reads per operand
-          i32x2_t v[NR];
-#pragma unroll
-          for (int t = 0; t < NR; ++t) {
-            // int8: K rows 32kk + 16hi + 8t + {0..7}; fp8: the two 16-byte
-            // pieces of a lane come from the two halves of the 64-wide step
-            const uint32_t k = (NR == 2) ? 32 * kk + 16 * hi + 8 * t + (L >> 1)
-                                         : 64 * kk + 32 * (t >> 1) + 16 * hi + 8 * (t & 1) + (L >> 1);
-            const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
-            v[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
-          }
-          if constexpr (NR == 2)
-            f.b[kk][j] = u32x4_t{(uint32_t)v[0][0], (uint32_t)v[0][1], (uint32_t)v[1][0],
-                                 (uint32_t)v[1][1]};
-          else
-            f.b[kk][j] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
-        }
-        if constexpr (T::SCALED)
-          f.sb[kk][j] = scaled ? lsb[(2 * kk + hi) * BN + wn * TN + j * 32 + l32] : 0x7fu;
-        else
-          f.sb[kk][j] = 0;
+      for (int t = 0; t < NR; ++t) {
+        // int8: K rows 32kk + 16hi + 8t + {0..7}; fp8: the two 16-byte
+        // pieces of a lane come from the two halves of the 64-wide step
+        const uint32_t k = (NR == 2) ? 32 * KK + 16 * hi + 8 * t + (L >> 1)
+                                     : 64 * KK + 32 * (t >> 1) + 16 * hi + 8 * (t & 1) + (L >> 1);
+        const lds_t* p = lb + k * RB + ((((colb >> 4) ^ swz_b(k))) << 4) + (colb & 8u);
+        v[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
       }
+      if constexpr (NR == 2)
+        f.b[J] = u32x4_t{(uint32_t)v[0][0], (uint32_t)v[0][1], (uint32_t)v[1][0], (uint32_t)v[1][1]};
+      else
+        f.b[J] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
     }
+    if constexpr (T::SCALED)
+      f.sb[J] = scaled ? lsb[(2 * KK + hi) * BN + wn * TN + J * 32 + l32] : 0x7fu;
+    else
+      f.sb[J] = 0;
   }
 
-  __device__ static __forceinline__ void mfma_frags(Acc (&acc)[FM][FN], const Frags& f) {
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          mfma32<AB>(acc[i][j], f.b[kk][j], f.a[kk][i], f.sb[kk][j], f.sa[kk][i]);
+  // Fragment load X of K step KK: A fragments 0..FM-1, then B fragments 0..FN-1.
+  static constexpr int NLK = FM + FN;       // fragment loads per K step
+  static constexpr int NMK = FM * FN;       // MFMAs per K step
+  static constexpr int NMF = KSTEPS * NMK;  // MFMAs per stage
+
+  template <int S, int KK, int X>
+  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn,
+                                                  uint32_t scaled) {
+    if constexpr (X < FM)
+      load_a<S, KK, X>(f, wm, scaled);
+    else
+      load_b<S, KK, X - FM>(f, wn, scaled);
+  }
+  template <int S, int KK>
+  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn,
+                                                    uint32_t scaled) {
+    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value>(f, wm, wn, scaled); });
+  }
+
+  // MFMA Q of a K step (A fragment major).
+  template <int Q>
+  __device__ static __forceinline__ void mfma_one(Acc (&acc)[FM][FN], const KFrag& f) {
+    constexpr int I = Q / FN, J = Q % FN;
+    mfma32<AB>(acc[I][J], f.b[J], f.a[I], f.sb[J], f.sa[I]);
+  }
+
+  // The DMA instructions that MFMA slot Q of a stage carries: the LPS
+  // instructions dealt out evenly over the NMF slots.  A wave blocks while
+  // it issues a DMA instruction and its MFMA pipe drains meanwhile, so each
+  // one sits right behind an MFMA instead of in a burst.
+  template <int SD, int Q, bool FULL>
+  __device__ static __forceinline__ void slot_dma(const Ctx& c, const Dma& d, const Soff& so) {
+    static_for_range<(Q * LPS) / NMF, ((Q + 1) * LPS) / NMF>(
+        [&](auto x) { dma_one<SD, decltype(x)::value, FULL>(c, d, so); });
   }
 
   template <int N>
@@ -358,39 +533,168 @@ struct DmaKernel {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   }
 
-  // One K step; I counts steps modulo the unroll: stage kt lives in buffer
-  // I % STAGES, its fragments in register set `cur`.  The step makes stage
-  // kt+1 resident (own DMA complete, then a barrier, which also tells that
-  // every wave is done with the buffer the next DMA overwrites), issues the
-  // DMA of stage kt+STAGES-1, reads stage kt+1's fragments into `nxt`, and
-  // runs stage kt's MFMAs from `cur` while those reads are in flight.
-  template <int I>
-  __device__ static __forceinline__ void step(Acc (&acc)[FM][FN], Frags& cur, Frags& nxt,
-                                              const Ctx& c, uint32_t k0, uint32_t kt, uint32_t nk,
-                                              uint32_t wm, uint32_t wn) {
-    constexpr int S = I % STAGES;
-    if (kt >= nk) return;
-    if constexpr (STAGES == 2) {
-      // Two buffers leave no room to read ahead: wait for stage kt, then
-      // refill the other buffer while computing from this one.
-      wait_vm<0>();
+  // Two schedules.  Every step runs its MFMAs unconditionally: the stage
+  // count is padded up to the unroll (padding stages hold zeros) and the
+  // last unroll group is peeled with its DMA and wait pattern fixed at
+  // compile time, so the accumulators never pass through a branch and the
+  // steady state carries no per-instruction conditions.
+  //
+  // Stage prefetch (4 stages): the operands of the whole current stage are
+  // in registers; the MFMAs of stage kt carry the DMA of stage kt+3 and the
+  // LDS reads of stage kt+1's operands.
+  //
+  // K-step prefetch (2 or 3 stages, for tiles whose stage operands do not
+  // fit twice in registers): the MFMAs of K step kk carry the LDS reads of
+  // K step kk+1 of the same stage and the stage's share of DMA.
+  static constexpr bool STAGE_PREFETCH = (STAGES == 4);
+  static constexpr int UNR = STAGES;  // steps per loop trip: buffer index stays compile-time
+  __host__ __device__ __forceinline__ static uint32_t padded_stages(uint32_t nk) {
+    return (nk + UNR - 1) / UNR * UNR;
+  }
+  // A task runs the unchecked DMA offsets when no stage is partial or padding.
+  __host__ __device__ __forceinline__ static bool full_task(uint32_t k0, uint32_t k1) {
+    const uint32_t nk = (k1 - k0) / BK;
+    return (k1 - k0) % BK == 0 && nk % UNR == 0;
+  }
+
+  struct SFrag {
+    KFrag k[KSTEPS];
+  };
+
+  // WAITN: outstanding DMA instructions allowed at the top of the step (-1:
+  // no wait and no barrier, the last step of the task).
+  template <int I, bool FULL, bool DMA, int WAITN, bool LOAD>
+  __device__ static __forceinline__ void step_stage(Acc (&acc)[FM][FN], const SFrag& cur,
+                                                    SFrag& nxt, const Ctx& c, const Dma& d,
+                                                    uint32_t kt, uint32_t wm, uint32_t wn,
+                                                    LoopTrace& tr) {
+    static_assert(STAGES == 4, "stage prefetch runs 4 buffers");
+    constexpr int S = I % STAGES, SD = (S + 3) % STAGES, SL = (S + 1) % STAGES;
+    // Issued so far: stages up to kt+2.  Stage kt+1 resident: own DMA done,
+    // then the barrier (which also tells that every wave has finished
+    // reading stage kt-1, whose buffer the DMA below refills).
+    tr.top();
+    if constexpr (WAITN >= 0) {
+      wait_vm<WAITN>();
       barrier_lds();
-      if (kt + 1 < nk) issue<(S + 1) % STAGES>(c, k0 + (kt + 1) * BK);
-      load_frags<S>(cur, wm, wn, c.scaled);
-      mfma_frags(acc, cur);
-    } else {
-      // stages issued so far: up to kt + STAGES - 2
-      if (kt + 1 < nk) {
-        if (kt + STAGES - 2 < nk)
-          wait_vm<LPS * (STAGES - 3)>();
-        else
-          wait_vm<0>();
-      }
-      barrier_lds();
-      if (kt + STAGES - 1 < nk) issue<(S + STAGES - 1) % STAGES>(c, k0 + (kt + STAGES - 1) * BK);
-      if (kt + 1 < nk) load_frags<(S + 1) % STAGES>(nxt, wm, wn, c.scaled);
-      mfma_frags(acc, cur);
     }
+    tr.released();
+    const Soff so = stage_soff(c, c.k0 + (kt + 3) * BK);
+    constexpr int NL = KSTEPS * NLK;
+    static_for<NMF>([&](auto q) {
+      constexpr int Q = decltype(q)::value;
+      mfma_one<Q % NMK>(acc, cur.k[Q / NMK]);
+      if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
+      if constexpr (LOAD) {
+        static_for_range<(Q * NL) / NMF, ((Q + 1) * NL) / NMF>([&](auto x) {
+          constexpr int X = decltype(x)::value;
+          load_one<SL, X / NLK, X % NLK>(nxt.k[X / NLK], wm, wn, c.scaled);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  template <int I, bool FULL, bool DMA, int WAITN>
+  __device__ static __forceinline__ void step_kstep(Acc (&acc)[FM][FN], const Ctx& c,
+                                                    const Dma& d, uint32_t kt, uint32_t wm,
+                                                    uint32_t wn, LoopTrace& tr) {
+    constexpr int S = I % STAGES, SD = (S + STAGES - 1) % STAGES;
+    // Issued so far: stages up to kt+STAGES-2.  Stage kt resident.
+    tr.top();
+    wait_vm<WAITN>();
+    barrier_lds();
+    tr.released();
+    const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
+    KFrag g0, g1;
+    load_kstep<S, 0>(g0, wm, wn, c.scaled);
+    static_for<NMF>([&](auto q) {
+      constexpr int Q = decltype(q)::value;
+      constexpr int KK = Q / NMK, R = Q % NMK;
+      mfma_one<R>(acc, (KK & 1) ? g1 : g0);
+      if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
+      if constexpr (KK + 1 < KSTEPS) {
+        static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
+          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn, c.scaled);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // The K loop of one task: nkp (padded, >= UNR) stages from K index c.k0.
+  template <bool FULL>
+  __device__ static __forceinline__ void kloop(Acc (&acc)[FM][FN], const Ctx& c, uint32_t nkp,
+                                               uint32_t wm, uint32_t wn, uint64_t* trace_out) {
+    LoopTrace tr;
+    tr.begin();
+    const Dma d = make_dma<FULL>(c);
+    issue<0, FULL>(c, d, c.k0);
+    if constexpr (STAGES > 2) issue<1, FULL>(c, d, c.k0 + BK);
+    uint32_t kt = 0;
+    if constexpr (STAGE_PREFETCH) {
+      issue<2, FULL>(c, d, c.k0 + 2 * BK);
+      wait_vm<2 * LPS>();  // stage 0 resident
+      barrier_lds();
+      SFrag f0, f1;
+      static_for<KSTEPS>([&](auto kk) {
+        constexpr int KK = decltype(kk)::value;
+        load_kstep<0, KK>(f0.k[KK], wm, wn, c.scaled);
+      });
+      tr.prologue_done();
+      for (; kt + 4 < nkp; kt += 4) {
+        step_stage<0, FULL, true, LPS, true>(acc, f0, f1, c, d, kt, wm, wn, tr);
+        step_stage<1, FULL, true, LPS, true>(acc, f1, f0, c, d, kt + 1, wm, wn, tr);
+        step_stage<2, FULL, true, LPS, true>(acc, f0, f1, c, d, kt + 2, wm, wn, tr);
+        step_stage<3, FULL, true, LPS, true>(acc, f1, f0, c, d, kt + 3, wm, wn, tr);
+      }
+      // last group: stage kt+3 is the last to load; nothing past it
+      step_stage<0, FULL, true, LPS, true>(acc, f0, f1, c, d, kt, wm, wn, tr);
+      step_stage<1, FULL, false, LPS, true>(acc, f1, f0, c, d, kt + 1, wm, wn, tr);
+      step_stage<2, FULL, false, 0, true>(acc, f0, f1, c, d, kt + 2, wm, wn, tr);
+      step_stage<3, FULL, false, -1, false>(acc, f1, f0, c, d, kt + 3, wm, wn, tr);
+    } else {
+      constexpr int W = (STAGES == 3) ? LPS : 0;
+      tr.prologue_done();
+      for (; kt + STAGES < nkp; kt += STAGES) {
+        step_kstep<0, FULL, true, W>(acc, c, d, kt, wm, wn, tr);
+        step_kstep<1, FULL, true, W>(acc, c, d, kt + 1, wm, wn, tr);
+        if constexpr (STAGES > 2) step_kstep<2, FULL, true, W>(acc, c, d, kt + 2, wm, wn, tr);
+      }
+      // last group: only its first step has a stage left to issue
+      step_kstep<0, FULL, true, W>(acc, c, d, kt, wm, wn, tr);
+      if constexpr (STAGES > 2) {
+        step_kstep<1, FULL, false, W>(acc, c, d, kt + 1, wm, wn, tr);
+        step_kstep<2, FULL, false, 0>(acc, c, d, kt + 2, wm, wn, tr);
+      } else {
+        step_kstep<1, FULL, false, 0>(acc, c, d, kt + 1, wm, wn, tr);
+      }
+    }
+    // every wave is done with the stage buffers before the next task's
+    // prologue refills them
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_lds();
+    tr.finish(trace_out);
+  }
+
+  // One task: K loop (if any), split-K fix-up, epilogue.
+  template <bool FULL>
+  __device__ static __forceinline__ void task(const GemmArgs& a, const Ctx& c, const Task& tk,
+                                              uint32_t s, uint32_t t, uint32_t nk, uint32_t wm,
+                                              uint32_t wn) {
+    Acc acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+    if (nk > 0) kloop<FULL>(acc, c, padded_stages(nk), wm, wn, a.trace);
+    if (!Epi::fixup(a, acc, s, t)) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
   }
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
@@ -407,6 +711,8 @@ struct DmaKernel {
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     c.ldb_bytes = a.ldb * ES;
     c.ldsb = a.ldsb;
+    c.ldb_bytes32 = (uint32_t)c.ldb_bytes;
+    c.ldsb32 = (uint32_t)a.ldsb;
     const uint32_t wm = c.wave / WN, wn = c.wave % WN;
 
     for (uint32_t u = logical_wg(a.remap); u < units; u += gridDim.x) {
@@ -435,57 +741,14 @@ struct DmaKernel {
       c.scaled = (T::SCALED && a.sa != nullptr && a.sb != nullptr) ? 1u : 0u;
       c.sa_tile = c.scaled ? a.sa + tk.row0 * a.ldsa : nullptr;
       c.sb_tile = c.scaled ? a.sb + (int64_t)tk.n * BN : nullptr;
+      c.k0 = k0;
       c.kend = k1;
       lane_setup(c.ln, c.wave, threadIdx.x & 63u, tk.rows_valid, tk.n, a.N, a.lda, c.ldb_bytes,
                  a.ldsa, a.ldsb);
-
-      Acc acc[FM][FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-
-      if (nk > 0) {
-        issue<0>(c, k0);
-        if (STAGES > 2 && 1 < nk) issue<1 % STAGES>(c, k0 + BK);
-        if (STAGES > 3 && 2 < nk) issue<2 % STAGES>(c, k0 + 2 * BK);
-        Frags f0, f1;
-        if constexpr (STAGES > 2) {
-          // stage 0 resident and in registers before the first step
-          if (nk - 1 >= (uint32_t)(STAGES - 2))
-            wait_vm<LPS * (STAGES - 2)>();
-          else
-            wait_vm<0>();
-          barrier_lds();
-          load_frags<0>(f0, wm, wn, c.scaled);
-        }
-        // unrolled so that buffer index and register set are compile-time
-        constexpr int UNR = (STAGES % 2 == 0) ? STAGES : 2 * STAGES;
-        for (uint32_t kt = 0; kt < nk; kt += UNR) {
-          step<0>(acc, f0, f1, c, k0, kt, nk, wm, wn);
-          step<1>(acc, f1, f0, c, k0, kt + 1, nk, wm, wn);
-          if constexpr (UNR > 2) {
-            step<2>(acc, f0, f1, c, k0, kt + 2, nk, wm, wn);
-            step<3>(acc, f1, f0, c, k0, kt + 3, nk, wm, wn);
-          }
-          if constexpr (UNR > 4) {
-            step<4>(acc, f0, f1, c, k0, kt + 4, nk, wm, wn);
-            step<5>(acc, f1, f0, c, k0, kt + 5, nk, wm, wn);
-          }
-        }
-        // every wave is done with the stage buffers before the next task's
-        // prologue refills them
-        __builtin_amdgcn_s_waitcnt(0);
-        barrier_lds();
-      }
-
-      if (!Epi::fixup(a, acc, s, t)) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
+      if (nk > 0 && full_task(k0, k1))
+        task<true>(a, c, tk, s, t, nk, wm, wn);
+      else
+        task<false>(a, c, tk, s, t, nk, wm, wn);
     }
   }
 };

@@ -100,7 +100,12 @@ void check(const Problem& p) {
       const int64_t bidx = GROUPED ? 0 : tk.idx;
       const int64_t a_tile = (bidx * p.strideA + tk.row0 * p.lda) * ES;  // bytes from A
       const int64_t b_tile = ((int64_t)tk.idx * p.strideB + (int64_t)tk.n * BN) * ES;
-      for (uint32_t kt = 0; kt < nk; ++kt) {
+      // a task without partial or padding stages runs the precomputed lane
+      // offsets: they must equal the checked ones at every stage
+      const bool full = nk > 0 && KN::full_task(k0, k1);
+      auto same = [](uint32_t u, uint32_t v) { return u == v || (u >= kOob && v >= kOob); };
+      // padding stages (past nk, up to the unroll) must access nothing
+      for (uint32_t kt = 0; kt < KN::padded_stages(nk); ++kt) {
         const uint32_t kb0 = k0 + kt * BK;
         std::vector<int> covA(BM * 8, 0), covB(BK * KN::NCH, 0);
         std::vector<int> covSA(BM, 0), covSB(4 * BN, 0);
@@ -114,6 +119,7 @@ void check(const Problem& p) {
               REQUIRE(lds + 16 <= (uint32_t)KN::A_BYTES, "A lds %u", lds);
               const auto x = KN::a_access(ln, i, kb0, k1);
               ++g_checked;
+              if (full) REQUIRE(same(KN::full_voff(ln, i, p.scaled), x.voff), "A full voff");
               if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled A lane in range"); continue; }
               REQUIRE(x.voff < kOob, "A voff %u", x.voff);
               const int64_t addr = a_tile + (int64_t)kb0 * ES + x.voff;  // from batch base
@@ -139,6 +145,8 @@ void check(const Problem& p) {
               REQUIRE(lds + 16 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES), "B lds %u", lds);
               const auto x = KN::b_access(ln, i, kb0, k1);
               ++g_checked;
+              if (full)
+                REQUIRE(same(KN::full_voff(ln, KN::A_IPW + i, p.scaled), x.voff), "B full voff");
               if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled B lane in range"); continue; }
               REQUIRE(x.voff < kOob, "B voff %u", x.voff);
               const int64_t rel = b_tile - (int64_t)tk.idx * p.strideB * ES +
@@ -160,8 +168,11 @@ void check(const Problem& p) {
               for (int i = 0; i < KN::SA_IPW; ++i) {
                 const uint32_t lds = KN::sa_lds(w, i) + lane * 4;
                 REQUIRE(lds + 4 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES), "SA lds");
-                const auto x = KN::sa_access(ln, i);
+                const auto x = KN::sa_access(ln, i, kb0, k1);
                 ++g_checked;
+                if (full)
+                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + i, true), x.voff),
+                          "SA full voff");
                 if (!x.ok) continue;
                 const int64_t addr = tk.row0 * a.ldsa + kb0 / 32 + x.voff;
                 const int64_t R = addr / a.ldsa, c = addr % a.ldsa;
@@ -172,8 +183,12 @@ void check(const Problem& p) {
               for (int i = 0; i < KN::SB_IPW; ++i) {
                 const uint32_t lds = KN::sb_lds(w, i) + lane * 4;
                 REQUIRE(lds + 4 <= (uint32_t)KN::STAGE_BYTES, "SB lds");
-                const auto x = KN::sb_access(ln, i);
+                const auto x = KN::sb_access(ln, i, kb0, k1);
                 ++g_checked;
+                if (full)
+                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + KN::SA_IPW + i, true),
+                               x.voff),
+                          "SB full voff");
                 if (!x.ok) continue;
                 const int64_t addr = (int64_t)tk.n * BN + (int64_t)(kb0 / 32) * a.ldsb + x.voff;
                 const int64_t R = addr / a.ldsb, c = addr % a.ldsb;
@@ -199,10 +214,10 @@ void check(const Problem& p) {
           }
         if (KN::T::SCALED && p.scaled) {
           for (int r = 0; r < BM; ++r)
-            REQUIRE(covSA[r] == ((uint32_t)r < tk.rows_valid ? 1 : 0), "SA coverage %d", r);
+            REQUIRE(covSA[r] == ((uint32_t)r < tk.rows_valid && kb0 < k1 ? 1 : 0), "SA coverage %d", r);
           for (int e = 0; e < 4; ++e)
             for (int c = 0; c < BN; ++c)
-              REQUIRE(covSB[e * BN + c] == (tk.n * BN + c < a.N ? 1 : 0), "SB coverage");
+              REQUIRE(covSB[e * BN + c] == (tk.n * BN + c < a.N && kb0 < k1 ? 1 : 0), "SB coverage");
         }
       }
     }
