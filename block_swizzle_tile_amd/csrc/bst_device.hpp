@@ -352,103 +352,191 @@ struct Epilogue {
     }
     __syncthreads();
     if (last_flag == 0) return false;
+    // Sum in slice order.  A whole slice's partials (two slices' when the
+    // wave's part of the tile is small enough to hold twice in registers)
+    // are requested before any is added, so the loads overlap instead of
+    // waiting one by one.
+    constexpr uint32_t PAIR = (FM * FN <= 4) ? 2u : 1u;
+    Acc sum[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        Acc sum;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum[e] = 0;
-        for (uint32_t ss = 0; ss < a.split; ++ss) {
-          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-              reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)ss * a.tile_cap + t) * tile_bytes,
-              (short)0, (int)tile_bytes, 0x00020000);
+        for (int e = 0; e < 16; ++e) sum[i][j][e] = 0;
+    for (uint32_t ss = 0; ss < a.split; ss += PAIR) {
+      const bool two = PAIR == 2 && ss + 1 < a.split;
+      u32x4_t v0[FM][FN][4], v1[FM][FN][4];
+      const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)ss * a.tile_cap + t) * tile_bytes,
+          (short)0, (int)tile_bytes, 0x00020000);
+      // the second slice's descriptor is range-limited to 0 bytes when absent
+      const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint8_t*>(a.ws_part) +
+              ((size_t)(two ? ss + 1 : ss) * a.tile_cap + t) * tile_bytes,
+          (short)0, two ? (int)tile_bytes : 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                r, wave_off + (i * FN + j) * 4096u + q * 1024u, 0, kDeviceScope);
+            const uint32_t off = wave_off + (i * FN + j) * 4096u + q * 1024u;
+            v0[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, kDeviceScope);
+            if constexpr (PAIR == 2)
+              v1[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, kDeviceScope);
+            else
+              v1[i][j][q] = u32x4_t{0, 0, 0, 0};
+          }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t x = v[e];
-              if constexpr (T::IS_INT)
-                sum[4 * q + e] += __builtin_bit_cast(int, x);
-              else
-                sum[4 * q + e] += __builtin_bit_cast(float, x);
+              const uint32_t x0 = v0[i][j][q][e], x1 = v1[i][j][q][e];
+              if constexpr (T::IS_INT) {
+                sum[i][j][4 * q + e] += __builtin_bit_cast(int, x0);
+                if (two) sum[i][j][4 * q + e] += __builtin_bit_cast(int, x1);
+              } else {
+                sum[i][j][4 * q + e] += __builtin_bit_cast(float, x0);
+                if (two) sum[i][j][4 * q + e] += __builtin_bit_cast(float, x1);
+              }
             }
-          }
-        }
-        acc[i][j] = sum;
-      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = sum[i][j];
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.ws_count[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
 
-  // Output of one 32x32 sub-tile: lane holds rows l32, columns 8g + 4*hi + {0..3}.
-  __device__ __attribute__((always_inline)) static void store_out(const GemmArgs& a, const Task& tk, const Acc& v, int i, int j,
-                                   uint32_t wm, uint32_t wn) {
+  // Two output elements packed into one dword, rounded to nearest even
+  // (the gfx950 conversions round that way in the default mode).
+  template <int OUT>
+  __device__ static __forceinline__ uint32_t pack2(float x, float y) {
+    if constexpr (OUT == OUT_F16)
+      return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y) << 16);
+    else
+      return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
+  }
+
+  // Stores of a wave's sub-tiles as output kind OUT; lane holds rows l32,
+  // columns 8g + 4*hi + {0..3} of each 32x32 sub-tile.  DEQ applies the
+  // per-row and per-column scales, out = (float(acc) * row) * column.  FULL:
+  // every row and column of the tile is inside the problem, so each lane
+  // writes its 4 consecutive values with one vector store and no mask.
+  template <int OUT, bool DEQ, bool FULL>
+  __device__ static __forceinline__ void store_as(const GemmArgs& a, const Task& tk,
+                                                  const Acc (&acc)[FM][FN], uint32_t wm,
+                                                  uint32_t wn) {
+    constexpr int OS = (OUT == OUT_F16 || OUT == OUT_BF16) ? 2 : 4;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
-    const uint32_t ml = wm * TM + i * 32 + l32;
-    if (ml >= tk.rows_valid) return;
-    const int64_t grow = tk.row0 + ml;
-    const bool deq = a.row_scale != nullptr;
-    const float rs = deq ? a.row_scale[grow] : 1.0f;
-    uint8_t* crow = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + grow * a.ldc) *
-                             (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16 ? 2 : 4);
+    uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
+                            (int64_t)tk.n * BN) * OS;
+    const float* csb = nullptr;
+    if constexpr (DEQ)
+      csb = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + (int64_t)tk.n * BN;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;
-      if (nl >= tk.nAct) continue;
-      const uint32_t gn = tk.n * BN + nl;
-      float f[4];
-      int32_t iv[4];
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t ml = wm * TM + i * 32 + l32;
+      if (!FULL && ml >= tk.rows_valid) continue;
+      uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
+      float rs = 1.0f;
+      if constexpr (DEQ) rs = a.row_scale[tk.row0 + ml];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (T::IS_INT) {
-          iv[r] = v[4 * g + r];
-          f[r] = (float)iv[r];
-        } else {
-          f[r] = v[4 * g + r];
-          iv[r] = 0;
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;  // column inside the tile
+          if (!FULL && nl >= tk.nAct) continue;
+          const bool whole = FULL || nl + 4 <= tk.nAct;
+          float f[4];
+          int32_t iv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const auto x = acc[i][j][4 * g + r];
+            if constexpr (T::IS_INT) {
+              iv[r] = x;
+              f[r] = (float)iv[r];
+            } else {
+              f[r] = x;
+              iv[r] = 0;
+            }
+          }
+          if constexpr (DEQ) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float c = (whole || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
+              f[r] = (f[r] * rs) * c;
+            }
+          }
+          uint8_t* p = crow + nl * OS;
+          if (whole) {
+            if constexpr (OS == 2)
+              *(u32x2_t*)__builtin_assume_aligned(p, 8) =
+                  u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
+            else if constexpr (OUT == OUT_F32)
+              *(f32x4_t*)__builtin_assume_aligned(p, 16) = f32x4_t{f[0], f[1], f[2], f[3]};
+            else
+              *(i32x4_t*)__builtin_assume_aligned(p, 16) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (nl + r >= tk.nAct) continue;
+              if constexpr (OS == 2)
+                ((uint16_t*)p)[r] = (uint16_t)pack2<OUT>(f[r], 0.0f);
+              else if constexpr (OUT == OUT_F32)
+                ((float*)p)[r] = f[r];
+              else
+                ((int32_t*)p)[r] = iv[r];
+            }
+          }
         }
-      }
-      if (deq) {
-        const float* cs = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + gn;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float c = (nl + r < tk.nAct) ? cs[r] : 0.0f;
-          f[r] = (f[r] * rs) * c;
-        }
-      }
-      const bool full = nl + 4 <= tk.nAct;
-      if (a.cdtype == OUT_F16 || a.cdtype == OUT_BF16) {
-        uint16_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = a.cdtype == OUT_F16 ? f32_to_f16_rne(f[r]) : f32_to_bf16_rne(f[r]);
-        uint16_t* p = reinterpret_cast<uint16_t*>(crow) + gn;
-        if (full) {
-          *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-        } else {
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = h[r];
-        }
-      } else if (a.cdtype == OUT_F32) {
-        float* p = reinterpret_cast<float*>(crow) + gn;
-        if (full) *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
+    }
+  }
+
+  template <bool DEQ, bool FULL>
+  __device__ static __forceinline__ void store_kind(const GemmArgs& a, const Task& tk,
+                                                    const Acc (&acc)[FM][FN], uint32_t wm,
+                                                    uint32_t wn) {
+    if (a.cdtype == OUT_F16)
+      store_as<OUT_F16, DEQ, FULL>(a, tk, acc, wm, wn);
+    else if (a.cdtype == OUT_BF16)
+      store_as<OUT_BF16, DEQ, FULL>(a, tk, acc, wm, wn);
+    else if (a.cdtype == OUT_F32)
+      store_as<OUT_F32, DEQ, FULL>(a, tk, acc, wm, wn);
+    else if constexpr (T::IS_INT && !DEQ)
+      store_as<OUT_I32, false, FULL>(a, tk, acc, wm, wn);
+  }
+
+  // The wave's whole output: one dispatch per task on the output kind, the
+  // dequant and whether the tile is whole, then straight-line stores.
+  // Dequantised outputs exist for int8 operands only.
+  __device__ static __forceinline__ void store_tile(const GemmArgs& a, const Task& tk,
+                                                    const Acc (&acc)[FM][FN], uint32_t wm,
+                                                    uint32_t wn) {
+    const bool full = tk.rows_valid >= (uint32_t)BM && tk.nAct >= (uint32_t)BN;
+    if constexpr (T::IS_INT) {
+      if (a.row_scale != nullptr) {
+        if (full)
+          store_kind<true, true>(a, tk, acc, wm, wn);
         else
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = f[r];
-      } else {  // OUT_I32
-        int32_t* p = reinterpret_cast<int32_t*>(crow) + gn;
-        if (full) *reinterpret_cast<i32x4_t*>(p) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
-        else
-          for (int r = 0; r < 4; ++r)
-            if (nl + r < tk.nAct) p[r] = iv[r];
+          store_kind<true, false>(a, tk, acc, wm, wn);
+        return;
       }
     }
+    if (full)
+      store_kind<false, true>(a, tk, acc, wm, wn);
+    else
+      store_kind<false, false>(a, tk, acc, wm, wn);
   }
 
 };
@@ -749,10 +837,7 @@ struct GemmKernel {
       }
 
       if (!Epi::fixup(a, acc, s, t)) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
+      Epi::store_tile(a, tk, acc, wm, wn);
     }
   }
 };

@@ -120,6 +120,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_range<0, N>(f);
 }
 
+// Shader-clock stamp for the BST_TRACE cycle accounting (0 otherwise).
+__device__ __forceinline__ uint64_t trace_stamp() {
+#ifdef BST_TRACE
+  return __builtin_amdgcn_s_memtime();
+#else
+  return 0;
+#endif
+}
+
 // Cycle accounting of the K loop (BST_TRACE builds only; empty otherwise):
 // time in the wait + barrier at the top of each step, and in the step bodies.
 struct LoopTrace {
@@ -681,7 +690,8 @@ struct DmaKernel {
   template <bool FULL>
   __device__ static __forceinline__ void task(const GemmArgs& a, const Ctx& c, const Task& tk,
                                               uint32_t s, uint32_t t, uint32_t nk, uint32_t wm,
-                                              uint32_t wn) {
+                                              uint32_t wn, uint64_t t_start) {
+    const uint64_t t_loop = trace_stamp();
     Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -690,14 +700,36 @@ struct DmaKernel {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
     if (nk > 0) kloop<FULL>(acc, c, padded_stages(nk), wm, wn, a.trace);
-    if (!Epi::fixup(a, acc, s, t)) return;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) Epi::store_out(a, tk, acc[i][j], i, j, wm, wn);
+    const uint64_t t_epi = trace_stamp();
+    uint64_t t_fix = t_epi;
+    if (Epi::fixup(a, acc, s, t)) {
+      t_fix = trace_stamp();
+      Epi::store_tile(a, tk, acc, wm, wn);
+    }
+#ifdef BST_TRACE
+    const uint64_t t_end = trace_stamp();
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint64_t t_done = trace_stamp();
+    if (a.trace != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
+      uint64_t* o = a.trace + 32 + (threadIdx.x >> 6) * 4;
+      o[0] += t_loop - t_start;  // task setup (first task: from kernel start)
+      o[1] += t_epi - t_loop;    // K loop
+      o[2] += t_end - t_epi;     // fix-up and epilogue
+      o[3] += 1;                 // tasks
+      uint64_t* q = a.trace + 64 + (threadIdx.x >> 6) * 4;
+      q[0] += t_fix - t_epi;     // fix-up
+      q[1] += t_end - t_fix;     // stores issued
+      q[2] += t_done - t_end;    // stores complete
+    }
+#else
+    (void)t_start;
+    (void)t_loop;
+    (void)t_epi;
+#endif
   }
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
+    uint64_t t_start = trace_stamp();
     GroupTable* gt = nullptr;
     uint32_t T_tiles = a.tiles;
     if constexpr (GROUPED) {
@@ -746,9 +778,10 @@ struct DmaKernel {
       lane_setup(c.ln, c.wave, threadIdx.x & 63u, tk.rows_valid, tk.n, a.N, a.lda, c.ldb_bytes,
                  a.ldsa, a.ldsb);
       if (nk > 0 && full_task(k0, k1))
-        task<true>(a, c, tk, s, t, nk, wm, wn);
+        task<true>(a, c, tk, s, t, nk, wm, wn, t_start);
       else
-        task<false>(a, c, tk, s, t, nk, wm, wn);
+        task<false>(a, c, tk, s, t, nk, wm, wn, t_start);
+      t_start = trace_stamp();
     }
   }
 };
