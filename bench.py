@@ -56,15 +56,19 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--tile", default="64x64")
     p.add_argument("--split", type=int, default=1)
-    p.add_argument("--offset", type=int, default=2)
+    p.add_argument("--offset", type=int, default=8)
     p.add_argument("--direction", default="zn")
     p.add_argument("--remap", type=int, default=1)
     p.add_argument("--grid", type=int, default=0)
-    p.add_argument("--mx-tile", default="128x128")
-    p.add_argument("--mx-split", type=int, default=2)
+    p.add_argument("--mx-tile", default="64x64")
+    p.add_argument("--mx-split", type=int, default=1)
     p.add_argument("--no-mx", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    p.add_argument("--l2-sweep", action="store_true",
+                   help="only run the fp16 workload under every swizzle setting (Zn / Nz offsets "
+                        "1, 2, 4, 8 and RASTER, XCD remap off / on) at the 256x128 and the 64x64 "
+                        "tile, --steps launches each, for per-setting rocprofv3 counters")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run plain 256 MiB device copies (the known-size reference that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -97,6 +101,29 @@ def time_launches(fn, steps, warmup):
     return total, total / steps
 
 
+def l2_sweep(args, bst, I, gpu, torch):
+    """Every swizzle setting on the fp16 1024x1024x2048 workload, in a fixed
+    order printed first as JSON (one kernel launch per step, no graph), so a
+    rocprofv3 run can attribute its per-dispatch counters to settings."""
+    w = I.workload("fp16_2k")
+    A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    cfgs = []
+    for tile in ((256, 128), (64, 64)):
+        for remap in (0, 1):
+            for d in ("zn", "nz"):
+                for off in (1, 2, 4, 8):
+                    cfgs.append({"tile": tile, "direction": d, "offset": off, "xcd_remap": remap})
+            cfgs.append({"tile": tile, "direction": "raster", "offset": 1, "xcd_remap": remap})
+    print(json.dumps({"l2_sweep": cfgs, "launches_each": args.steps}), flush=True)
+    for c in cfgs:
+        s = bst.make_sched(tile=c["tile"], offset=c["offset"], direction=c["direction"],
+                           split_k=1, xcd_remap=c["xcd_remap"])
+        for _ in range(args.steps):
+            bst.gemm(A, B, C, sched=s)
+        torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +154,10 @@ def main():
         if kind == "e4m3":
             return torch.from_numpy(a.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
         return torch.from_numpy(a).cuda()
+
+    if args.l2_sweep:
+        l2_sweep(args, bst, I, gpu, torch)
+        return
 
     # ---------------------------------------------------------- fp16 2k --
     w = I.workload("fp16_2k")
