@@ -548,15 +548,28 @@ struct DmaKernel {
   // compile time, so the accumulators never pass through a branch and the
   // steady state carries no per-instruction conditions.
   //
-  // Stage prefetch (4 stages): the operands of the whole current stage are
-  // in registers; the MFMAs of stage kt carry the DMA of stage kt+3 and the
-  // LDS reads of stage kt+1's operands.
+  // Ring (3 or 4 stages): the MFMAs of K step g carry the LDS reads of K
+  // step g+PD, which may lie in the next stage (resident from the top of
+  // the step on), and the step's share of the DMA of stage kt+STAGES-1.
+  // PD+1 K steps of operands live in registers, in a ring of sets.
   //
-  // K-step prefetch (2 or 3 stages, for tiles whose stage operands do not
-  // fit twice in registers): the MFMAs of K step kk carry the LDS reads of
-  // K step kk+1 of the same stage and the stage's share of DMA.
-  static constexpr bool STAGE_PREFETCH = (STAGES == 4);
+  // K-step (2 stages): the next stage is still in flight during a step, so
+  // the reads run inside the stage only: the MFMAs of K step kk carry the
+  // reads of K step kk+1.
   static constexpr int UNR = STAGES;  // steps per loop trip: buffer index stays compile-time
+  static constexpr int RING_K = UNR * KSTEPS;  // K steps per loop trip
+  // The ring's read-ahead: as far as 3 K steps (and never past the next
+  // stage), with a set count that divides the K steps of one trip so that
+  // every set index is a compile-time constant.
+  static constexpr int ring_pd() {
+    for (int dd = (KSTEPS < 3 ? KSTEPS : 3); dd > 1; --dd)
+      if (RING_K % (dd + 1) == 0) return dd;
+    return 1;
+  }
+  static constexpr int PD = ring_pd();
+  static constexpr int NSET = PD + 1;
+  static_assert(STAGES == 2 || (RING_K % NSET == 0 && PD <= KSTEPS), "ring shape");
+
   __host__ __device__ __forceinline__ static uint32_t padded_stages(uint32_t nk) {
     return (nk + UNR - 1) / UNR * UNR;
   }
@@ -566,38 +579,35 @@ struct DmaKernel {
     return (k1 - k0) % BK == 0 && nk % UNR == 0;
   }
 
-  struct SFrag {
-    KFrag k[KSTEPS];
-  };
-
-  // WAITN: outstanding DMA instructions allowed at the top of the step (-1:
-  // no wait and no barrier, the last step of the task).
-  template <int I, bool FULL, bool DMA, int WAITN, bool LOAD>
-  __device__ static __forceinline__ void step_stage(Acc (&acc)[FM][FN], const SFrag& cur,
-                                                    SFrag& nxt, const Ctx& c, const Dma& d,
-                                                    uint32_t kt, uint32_t wm, uint32_t wn,
-                                                    LoopTrace& tr) {
-    static_assert(STAGES == 4, "stage prefetch runs 4 buffers");
-    constexpr int S = I % STAGES, SD = (S + 3) % STAGES, SL = (S + 1) % STAGES;
-    // Issued so far: stages up to kt+2.  Stage kt+1 resident: own DMA done,
-    // then the barrier (which also tells that every wave has finished
-    // reading stage kt-1, whose buffer the DMA below refills).
+  // One step of the ring schedule.  WAITN: outstanding DMA instructions
+  // allowed at the top (-1: no wait and no barrier, the task's last step);
+  // LAST: skip the reads that would run past the task's last stage.
+  template <int I, bool FULL, bool DMA, int WAITN, bool LAST>
+  __device__ static __forceinline__ void step_ring(Acc (&acc)[FM][FN], KFrag (&f)[NSET],
+                                                   const Ctx& c, const Dma& d, uint32_t kt,
+                                                   uint32_t wm, uint32_t wn, LoopTrace& tr) {
+    constexpr int S = I % STAGES, SD = (S + STAGES - 1) % STAGES;
+    // Stage kt+1 resident: own DMA done, then the barrier (which also tells
+    // that every wave has finished reading stage kt-1, whose buffer the DMA
+    // below refills).
     tr.top();
     if constexpr (WAITN >= 0) {
       wait_vm<WAITN>();
       barrier_lds();
     }
     tr.released();
-    const Soff so = stage_soff(c, c.k0 + (kt + 3) * BK);
-    constexpr int NL = KSTEPS * NLK;
+    const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
-      mfma_one<Q % NMK>(acc, cur.k[Q / NMK]);
+      constexpr int KK = Q / NMK, R = Q % NMK;
+      constexpr int G = I * KSTEPS + KK;  // K step inside the trip
+      mfma_one<R>(acc, f[G % NSET]);
       if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
-      if constexpr (LOAD) {
-        static_for_range<(Q * NL) / NMF, ((Q + 1) * NL) / NMF>([&](auto x) {
-          constexpr int X = decltype(x)::value;
-          load_one<SL, X / NLK, X % NLK>(nxt.k[X / NLK], wm, wn, c.scaled);
+      constexpr int GL = G + PD;  // the K step whose operands are read now
+      if constexpr (!(LAST && GL >= RING_K)) {
+        constexpr int SB = (GL / KSTEPS) % STAGES, KL = GL % KSTEPS;
+        static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
+          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn, c.scaled);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -641,43 +651,48 @@ struct DmaKernel {
     issue<0, FULL>(c, d, c.k0);
     if constexpr (STAGES > 2) issue<1, FULL>(c, d, c.k0 + BK);
     uint32_t kt = 0;
-    if constexpr (STAGE_PREFETCH) {
-      issue<2, FULL>(c, d, c.k0 + 2 * BK);
-      wait_vm<2 * LPS>();  // stage 0 resident
+    if constexpr (STAGES > 2) {
+      if constexpr (STAGES == 4) {
+        issue<2, FULL>(c, d, c.k0 + 2 * BK);
+        wait_vm<2 * LPS>();  // stage 0 resident
+      } else {
+        wait_vm<LPS>();
+      }
       barrier_lds();
-      SFrag f0, f1;
-      static_for<KSTEPS>([&](auto kk) {
-        constexpr int KK = decltype(kk)::value;
-        load_kstep<0, KK>(f0.k[KK], wm, wn, c.scaled);
+      KFrag f[NSET];
+      static_for<PD>([&](auto g) {
+        constexpr int GG = decltype(g)::value;
+        load_kstep<0, GG>(f[GG], wm, wn, c.scaled);
       });
       tr.prologue_done();
-      for (; kt + 4 < nkp; kt += 4) {
-        step_stage<0, FULL, true, LPS, true>(acc, f0, f1, c, d, kt, wm, wn, tr);
-        step_stage<1, FULL, true, LPS, true>(acc, f1, f0, c, d, kt + 1, wm, wn, tr);
-        step_stage<2, FULL, true, LPS, true>(acc, f0, f1, c, d, kt + 2, wm, wn, tr);
-        step_stage<3, FULL, true, LPS, true>(acc, f1, f0, c, d, kt + 3, wm, wn, tr);
+      constexpr int WM_ = (STAGES == 4) ? LPS : 0;  // steady-state wait
+      for (; kt + UNR < nkp; kt += UNR) {
+        step_ring<0, FULL, true, WM_, false>(acc, f, c, d, kt, wm, wn, tr);
+        step_ring<1, FULL, true, WM_, false>(acc, f, c, d, kt + 1, wm, wn, tr);
+        step_ring<2, FULL, true, WM_, false>(acc, f, c, d, kt + 2, wm, wn, tr);
+        if constexpr (STAGES == 4) step_ring<3, FULL, true, WM_, false>(acc, f, c, d, kt + 3, wm, wn, tr);
       }
-      // last group: stage kt+3 is the last to load; nothing past it
-      step_stage<0, FULL, true, LPS, true>(acc, f0, f1, c, d, kt, wm, wn, tr);
-      step_stage<1, FULL, false, LPS, true>(acc, f1, f0, c, d, kt + 1, wm, wn, tr);
-      step_stage<2, FULL, false, 0, true>(acc, f0, f1, c, d, kt + 2, wm, wn, tr);
-      step_stage<3, FULL, false, -1, false>(acc, f1, f0, c, d, kt + 3, wm, wn, tr);
+      // last group: only its first step has a stage left to issue, and the
+      // last step waits for nothing
+      if constexpr (STAGES == 4) {
+        step_ring<0, FULL, true, LPS, false>(acc, f, c, d, kt, wm, wn, tr);
+        step_ring<1, FULL, false, LPS, false>(acc, f, c, d, kt + 1, wm, wn, tr);
+        step_ring<2, FULL, false, 0, false>(acc, f, c, d, kt + 2, wm, wn, tr);
+        step_ring<3, FULL, false, -1, true>(acc, f, c, d, kt + 3, wm, wn, tr);
+      } else {
+        step_ring<0, FULL, true, 0, false>(acc, f, c, d, kt, wm, wn, tr);
+        step_ring<1, FULL, false, 0, false>(acc, f, c, d, kt + 1, wm, wn, tr);
+        step_ring<2, FULL, false, -1, true>(acc, f, c, d, kt + 2, wm, wn, tr);
+      }
     } else {
-      constexpr int W = (STAGES == 3) ? LPS : 0;
       tr.prologue_done();
       for (; kt + STAGES < nkp; kt += STAGES) {
-        step_kstep<0, FULL, true, W>(acc, c, d, kt, wm, wn, tr);
-        step_kstep<1, FULL, true, W>(acc, c, d, kt + 1, wm, wn, tr);
-        if constexpr (STAGES > 2) step_kstep<2, FULL, true, W>(acc, c, d, kt + 2, wm, wn, tr);
+        step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
+        step_kstep<1, FULL, true, 0>(acc, c, d, kt + 1, wm, wn, tr);
       }
       // last group: only its first step has a stage left to issue
-      step_kstep<0, FULL, true, W>(acc, c, d, kt, wm, wn, tr);
-      if constexpr (STAGES > 2) {
-        step_kstep<1, FULL, false, W>(acc, c, d, kt + 1, wm, wn, tr);
-        step_kstep<2, FULL, false, 0>(acc, c, d, kt + 2, wm, wn, tr);
-      } else {
-        step_kstep<1, FULL, false, 0>(acc, c, d, kt + 1, wm, wn, tr);
-      }
+      step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
+      step_kstep<1, FULL, false, 0>(acc, c, d, kt + 1, wm, wn, tr);
     }
     // every wave is done with the stage buffers before the next task's
     // prologue refills them
