@@ -60,8 +60,8 @@ def parse():
     p.add_argument("--direction", default="zn")
     p.add_argument("--remap", type=int, default=1)
     p.add_argument("--grid", type=int, default=0)
-    p.add_argument("--mx-tile", default="64x64")
-    p.add_argument("--mx-split", type=int, default=1)
+    p.add_argument("--mx-tile", default="128x128")
+    p.add_argument("--mx-split", type=int, default=2)
     p.add_argument("--no-mx", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")

@@ -32,11 +32,11 @@ bst_status fail(bst_status st, const char* fmt, ...) {
   return st;
 }
 
-int kernel_ab(bst_dtype ab) { return ab == BST_MXE4M3 ? AB_E4M3 : (int)ab; }
+int kernel_ab(bst_dtype ab) { return (int)ab; }
 
 const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped, bool dma) {
   const InstanceList lists[] = {instances_f16(), instances_bf16(), instances_i8(),
-                                instances_fp8()};
+                                instances_fp8(), instances_mxfp8()};
   for (const InstanceList& l : lists)
     for (int i = 0; i < l.count; ++i) {
       const Instance& in = l.begin[i];

@@ -225,13 +225,19 @@ struct Traits<AB_I8> {
   static constexpr int ES = 1, BK = 128, KBR = 8, MFMA_K = 32, FRAG_DW = 4;
   static constexpr bool IS_INT = true, SCALED = false;
 };
+// fp8 e4m3 operands: plain (every block scale 2^0, fed as the constant
+// 0x7f) and MX (e8m0 block scales from memory) are separate kernels, so that
+// neither carries a run-time test on the scales.
 template <>
 struct Traits<AB_E4M3> {
   static constexpr int ES = 1, BK = 128, KBR = 8, MFMA_K = 64, FRAG_DW = 8;
-  static constexpr bool IS_INT = false, SCALED = true;
+  static constexpr bool IS_INT = false, SCALED = false;
 };
 template <>
-struct Traits<AB_MXE4M3> : Traits<AB_E4M3> {};
+struct Traits<AB_MXE4M3> {
+  static constexpr int ES = 1, BK = 128, KBR = 8, MFMA_K = 64, FRAG_DW = 8;
+  static constexpr bool IS_INT = false, SCALED = true;
+};
 
 // One 32x32 MFMA step: acc(32 n x 32 m) += Bt(32 n x k) * At(k x 32 m).
 template <int AB, typename Acc, typename Frag>
@@ -760,7 +766,7 @@ struct GemmKernel {
           fa[i] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
                           (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         }
-        sca[i] = T::SCALED ? (ls[row] >> (8 * (2 * kk + hi))) & 0xffu : 0u;
+        sca[i] = T::SCALED ? (ls[row] >> (8 * (2 * kk + hi))) & 0xffu : 0x7fu;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -773,7 +779,7 @@ struct GemmKernel {
           fb[j] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
                           (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         }
-        scb[j] = T::SCALED ? (ls[BM + row] >> (8 * (2 * kk + hi))) & 0xffu : 0u;
+        scb[j] = T::SCALED ? (ls[BM + row] >> (8 * (2 * kk + hi))) & 0xffu : 0x7fu;
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)

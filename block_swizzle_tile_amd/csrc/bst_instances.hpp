@@ -13,7 +13,7 @@ namespace bst {
 using LaunchFn = hipError_t (*)(dim3, dim3, hipStream_t, const GemmArgs&);
 
 struct Instance {
-  int ab;  // AbKind (AB_MXE4M3 shares the AB_E4M3 kernels)
+  int ab;  // AbKind
   int bm, bn;
   bool grouped;
   bool dma;    // LDS-DMA family (else register-staged)
@@ -58,5 +58,6 @@ InstanceList instances_f16();
 InstanceList instances_bf16();
 InstanceList instances_i8();
 InstanceList instances_fp8();
+InstanceList instances_mxfp8();
 
 }  // namespace bst

@@ -249,7 +249,6 @@ struct DmaKernel {
     uint32_t k0;             // first K index of the task's slice
     uint32_t kend;
     uint32_t wave;
-    uint32_t scaled;         // fp8 with block scales (else every scale is 2^0)
     Lanes ln;
   };
 
@@ -352,7 +351,7 @@ struct DmaKernel {
   // Lane offset of DMA instruction X when the stage is entirely inside the
   // slice (host-callable, so the CPU check compares it with the checked
   // per-stage offsets).
-  __host__ __device__ __forceinline__ static uint32_t full_voff(const Lanes& ln, int X, bool scaled) {
+  __host__ __device__ __forceinline__ static uint32_t full_voff(const Lanes& ln, int X) {
     if (X < A_IPW) return ((ln.a_ok >> X) & 1u) ? ln.a_off[X] : kOob;
     if (X < A_IPW + B_IPW) {
       const int i = X - A_IPW;
@@ -360,10 +359,10 @@ struct DmaKernel {
     }
     if (X < A_IPW + B_IPW + SA_IPW) {
       const int i = X - A_IPW - B_IPW;
-      return (scaled && ((ln.sa_ok >> i) & 1u)) ? ln.sa_off[i] : kOob;
+      return ((ln.sa_ok >> i) & 1u) ? ln.sa_off[i] : kOob;
     }
     const int i = X - A_IPW - B_IPW - SA_IPW;
-    return (scaled && ((ln.sb_ok >> i) & 1u)) ? ln.sb_off[i] : kOob;
+    return ((ln.sb_ok >> i) & 1u) ? ln.sb_off[i] : kOob;
   }
 
   template <bool FULL>
@@ -372,12 +371,12 @@ struct DmaKernel {
     d.ra = make_desc(c.a_tile);
     d.rb = make_desc(c.b_tile);
     if constexpr (T::SCALED) {
-      d.rsa = make_desc(c.scaled ? c.sa_tile : c.a_tile);
-      d.rsb = make_desc(c.scaled ? c.sb_tile : c.a_tile);
+      d.rsa = make_desc(c.sa_tile);
+      d.rsb = make_desc(c.sb_tile);
     }
     if constexpr (FULL) {
 #pragma unroll
-      for (int x = 0; x < LPS; ++x) d.vo[x] = full_voff(c.ln, x, c.scaled != 0);
+      for (int x = 0; x < LPS; ++x) d.vo[x] = full_voff(c.ln, x);
     }
     return d;
   }
@@ -404,13 +403,11 @@ struct DmaKernel {
       dma16(d.rb, base + b_lds(c.wave, i), v, so.b);
     } else if constexpr (X < A_IPW + B_IPW + SA_IPW) {
       constexpr int i = X - A_IPW - B_IPW;
-      const uint32_t v =
-          FULL ? d.vo[X] : (c.scaled ? sa_access(c.ln, i, so.kb0, c.kend).voff : kOob);
+      const uint32_t v = FULL ? d.vo[X] : sa_access(c.ln, i, so.kb0, c.kend).voff;
       dma4(d.rsa, base + sa_lds(c.wave, i), v, so.sa);
     } else {
       constexpr int i = X - A_IPW - B_IPW - SA_IPW;
-      const uint32_t v =
-          FULL ? d.vo[X] : (c.scaled ? sb_access(c.ln, i, so.kb0, c.kend).voff : kOob);
+      const uint32_t v = FULL ? d.vo[X] : sb_access(c.ln, i, so.kb0, c.kend).voff;
       dma4(d.rsb, base + sb_lds(c.wave, i), v, so.sb);
     }
   }
@@ -433,7 +430,7 @@ struct DmaKernel {
   // LDS -> registers, one operand fragment at a time: A fragment I and B
   // fragment J of K step KK of stage buffer S, with their block scales.
   template <int S, int KK, int I>
-  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, uint32_t scaled) {
+  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
     const lds_t* lsa = base + A_BYTES + B_BYTES;
@@ -450,13 +447,13 @@ struct DmaKernel {
                        (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
     }
     if constexpr (T::SCALED)
-      f.sa[I] = scaled ? (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * KK + hi))) & 0xffu : 0x7fu;
+      f.sa[I] = (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * KK + hi))) & 0xffu;
     else
-      f.sa[I] = 0;
+      f.sa[I] = 0x7fu;  // 2^0 (the scale operand only matters to fp8 MFMAs)
   }
 
   template <int S, int KK, int J>
-  __device__ static __forceinline__ void load_b(KFrag& f, uint32_t wn, uint32_t scaled) {
+  __device__ static __forceinline__ void load_b(KFrag& f, uint32_t wn) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* lb = base + A_BYTES;
     const lds_t* lsb = base + A_BYTES + B_BYTES + SA_BYTES;
@@ -495,9 +492,9 @@ struct DmaKernel {
         f.b[J] = Frag{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
     }
     if constexpr (T::SCALED)
-      f.sb[J] = scaled ? lsb[(2 * KK + hi) * BN + wn * TN + J * 32 + l32] : 0x7fu;
+      f.sb[J] = lsb[(2 * KK + hi) * BN + wn * TN + J * 32 + l32];
     else
-      f.sb[J] = 0;
+      f.sb[J] = 0x7fu;
   }
 
   // Fragment load X of K step KK: A fragments 0..FM-1, then B fragments 0..FN-1.
@@ -506,17 +503,15 @@ struct DmaKernel {
   static constexpr int NMF = KSTEPS * NMK;  // MFMAs per stage
 
   template <int S, int KK, int X>
-  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn,
-                                                  uint32_t scaled) {
+  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn) {
     if constexpr (X < FM)
-      load_a<S, KK, X>(f, wm, scaled);
+      load_a<S, KK, X>(f, wm);
     else
-      load_b<S, KK, X - FM>(f, wn, scaled);
+      load_b<S, KK, X - FM>(f, wn);
   }
   template <int S, int KK>
-  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn,
-                                                    uint32_t scaled) {
-    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value>(f, wm, wn, scaled); });
+  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn) {
+    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value>(f, wm, wn); });
   }
 
   // MFMA Q of a K step (A fragment major).
@@ -607,7 +602,7 @@ struct DmaKernel {
       if constexpr (!(LAST && GL >= RING_K)) {
         constexpr int SB = (GL / KSTEPS) % STAGES, KL = GL % KSTEPS;
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn, c.scaled);
+          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -626,7 +621,7 @@ struct DmaKernel {
     tr.released();
     const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
     KFrag g0, g1;
-    load_kstep<S, 0>(g0, wm, wn, c.scaled);
+    load_kstep<S, 0>(g0, wm, wn);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
@@ -634,7 +629,7 @@ struct DmaKernel {
       if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
       if constexpr (KK + 1 < KSTEPS) {
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn, c.scaled);
+          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -662,7 +657,7 @@ struct DmaKernel {
       KFrag f[NSET];
       static_for<PD>([&](auto g) {
         constexpr int GG = decltype(g)::value;
-        load_kstep<0, GG>(f[GG], wm, wn, c.scaled);
+        load_kstep<0, GG>(f[GG], wm, wn);
       });
       tr.prologue_done();
       constexpr int WM_ = (STAGES == 4) ? LPS : 0;  // steady-state wait
@@ -785,9 +780,8 @@ struct DmaKernel {
       const int64_t bidx = GROUPED ? 0 : tk.idx;
       c.a_tile = a.A + (bidx * a.strideA + tk.row0 * a.lda) * ES;
       c.b_tile = a.B + ((int64_t)tk.idx * a.strideB + (int64_t)tk.n * BN) * ES;
-      c.scaled = (T::SCALED && a.sa != nullptr && a.sb != nullptr) ? 1u : 0u;
-      c.sa_tile = c.scaled ? a.sa + tk.row0 * a.ldsa : nullptr;
-      c.sb_tile = c.scaled ? a.sb + (int64_t)tk.n * BN : nullptr;
+      c.sa_tile = T::SCALED ? a.sa + tk.row0 * a.ldsa : nullptr;
+      c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
       c.k0 = k0;
       c.kend = k1;
       lane_setup(c.ln, c.wave, threadIdx.x & 63u, tk.rows_valid, tk.n, a.N, a.lda, c.ldb_bytes,

@@ -1,4 +1,4 @@
-// inst_fp8.hip -- compiled kernel instances for fp8 (e4m3, plain and MX-scaled) operands.
+// inst_fp8.hip -- compiled kernel instances for plain fp8 (e4m3, every block scale 2^0) operands.
 #include "bst_instances.hpp"
 
 namespace bst {

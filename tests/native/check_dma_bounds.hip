@@ -119,7 +119,7 @@ void check(const Problem& p) {
               REQUIRE(lds + 16 <= (uint32_t)KN::A_BYTES, "A lds %u", lds);
               const auto x = KN::a_access(ln, i, kb0, k1);
               ++g_checked;
-              if (full) REQUIRE(same(KN::full_voff(ln, i, p.scaled), x.voff), "A full voff");
+              if (full) REQUIRE(same(KN::full_voff(ln, i), x.voff), "A full voff");
               if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled A lane in range"); continue; }
               REQUIRE(x.voff < kOob, "A voff %u", x.voff);
               const int64_t addr = a_tile + (int64_t)kb0 * ES + x.voff;  // from batch base
@@ -146,7 +146,7 @@ void check(const Problem& p) {
               const auto x = KN::b_access(ln, i, kb0, k1);
               ++g_checked;
               if (full)
-                REQUIRE(same(KN::full_voff(ln, KN::A_IPW + i, p.scaled), x.voff), "B full voff");
+                REQUIRE(same(KN::full_voff(ln, KN::A_IPW + i), x.voff), "B full voff");
               if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled B lane in range"); continue; }
               REQUIRE(x.voff < kOob, "B voff %u", x.voff);
               const int64_t rel = b_tile - (int64_t)tk.idx * p.strideB * ES +
@@ -171,7 +171,7 @@ void check(const Problem& p) {
                 const auto x = KN::sa_access(ln, i, kb0, k1);
                 ++g_checked;
                 if (full)
-                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + i, true), x.voff),
+                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + i), x.voff),
                           "SA full voff");
                 if (!x.ok) continue;
                 const int64_t addr = tk.row0 * a.ldsa + kb0 / 32 + x.voff;
@@ -186,7 +186,7 @@ void check(const Problem& p) {
                 const auto x = KN::sb_access(ln, i, kb0, k1);
                 ++g_checked;
                 if (full)
-                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + KN::SA_IPW + i, true),
+                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + KN::SA_IPW + i),
                                x.voff),
                           "SB full voff");
                 if (!x.ok) continue;
@@ -292,15 +292,20 @@ int main() {
   run_grouped<AB_I8, 128, 128, 2, 2, 4>(g8);
   run_grouped<AB_I8, 256, 128, 2, 2, 3>(g8);
   run_grouped<AB_I8, 256, 256, 4, 2, 2>(g8);
-  // fp8: plain (no scales) and MX (K a multiple of 128)
-  std::vector<Problem> p8f = p8;
-  p8f.push_back(plain("mx", 256, 512, 1024, 0, 0, 1, 1, true));
-  p8f.push_back(plain("mxtail", 200, 144, 384, 128, 16, 2, 1, true));
-  p8f.push_back(plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true));
-  run_plain<AB_E4M3, 64, 64, 2, 2, 4>(p8f);
-  run_plain<AB_E4M3, 128, 128, 2, 2, 4>(p8f);
-  run_plain<AB_E4M3, 256, 128, 2, 2, 3>(p8f);
-  run_plain<AB_E4M3, 256, 256, 4, 2, 2>(p8f);
+  // fp8: plain (no scales; their kernels issue no scale DMA) and MX (K a
+  // multiple of 128, scales always present)
+  run_plain<AB_E4M3, 64, 64, 2, 2, 4>(p8);
+  run_plain<AB_E4M3, 128, 128, 2, 2, 4>(p8);
+  run_plain<AB_E4M3, 256, 128, 2, 2, 3>(p8);
+  run_plain<AB_E4M3, 256, 256, 4, 2, 2>(p8);
+  const std::vector<Problem> pmx = {plain("mx", 256, 512, 1024, 0, 0, 1, 1, true),
+                                    plain("mxtail", 200, 144, 384, 128, 16, 2, 1, true),
+                                    plain("mxsplit", 130, 96, 1024, 0, 0, 3, 1, true),
+                                    plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true)};
+  run_plain<AB_MXE4M3, 64, 64, 2, 2, 4>(pmx);
+  run_plain<AB_MXE4M3, 128, 128, 2, 2, 4>(pmx);
+  run_plain<AB_MXE4M3, 256, 128, 2, 2, 3>(pmx);
+  run_plain<AB_MXE4M3, 256, 256, 4, 2, 2>(pmx);
   if (g_fail) {
     printf("FAILED: %d violations (%lld accesses checked)\n", g_fail, g_checked);
     return 1;

@@ -5,7 +5,7 @@ does not inspect.  A vector-ALU write of an SGPR (readfirstlane, a spilled
 scalar reloaded with v_readlane) needs 5 wait states before a vector-memory
 instruction reads that SGPR, and a write of M0 needs 1 before an LDS DMA.  A
 DMA that reads a stale descriptor or offset goes to a wrong global address.
-This compiles the fp8 instances (the ones under the highest register
+This compiles the MX-fp8 instances (the ones under the highest register
 pressure) to gfx950 assembly and requires every `buffer_load ... lds` to sit
 right behind an `s_nop` of at least 4."""
 import os
@@ -16,12 +16,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_every_lds_dma_is_behind_five_wait_states(tmp_path):
-    asm = str(tmp_path / "inst_fp8.s")
+    asm = str(tmp_path / "inst_mxfp8.s")
     subprocess.check_call(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                            "-Wno-pass-failed", "-I", os.path.join(ROOT, "include"),
                            "--cuda-device-only", "-S",
-                           os.path.join(ROOT, "block_swizzle_tile_amd", "csrc", "inst_fp8.hip"),
+                           os.path.join(ROOT, "block_swizzle_tile_amd", "csrc", "inst_mxfp8.hip"),
                            "-o", asm], stderr=subprocess.DEVNULL)
     lines = [l.split(";")[0].strip() for l in open(asm)]
     lines = [l for l in lines if l and not l.startswith(".") and not l.endswith(":")]
