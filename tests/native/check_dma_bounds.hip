@@ -274,6 +274,8 @@ int main() {
   run_plain<AB_F16, 256, 128, 2, 2, 3>(p16);
   run_plain<AB_F16, 128, 256, 2, 2, 3>(p16);
   run_plain<AB_F16, 128, 192, 2, 2, 3>(p16);
+  run_plain<AB_F16, 128, 64, 2, 2, 4>(p16);
+  run_plain<AB_F16, 64, 128, 2, 2, 4>(p16);
   run_grouped<AB_F16, 128, 128, 2, 2, 4>(g16);
   // 8-bit operands: K and N multiples of 16
   const std::vector<Problem> p8 = {
@@ -303,6 +305,10 @@ int main() {
                                     plain("mxsplit", 130, 96, 1024, 0, 0, 3, 1, true),
                                     plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true)};
   run_plain<AB_MXE4M3, 64, 64, 2, 2, 4>(pmx);
+  run_plain<AB_MXE4M3, 128, 64, 2, 2, 4>(pmx);
+  run_plain<AB_MXE4M3, 64, 128, 2, 2, 4>(pmx);
+  run_plain<AB_E4M3, 128, 64, 2, 2, 4>(p8);
+  run_plain<AB_E4M3, 64, 128, 2, 2, 4>(p8);
   run_plain<AB_MXE4M3, 128, 128, 2, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 256, 128, 2, 2, 3>(pmx);
   run_plain<AB_MXE4M3, 256, 256, 4, 2, 2>(pmx);
