@@ -25,6 +25,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+CALIB_BYTES = 256 << 20   # the calibration copy moves this many bytes each way
 PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "i8": 5000.0}   # TFLOP/s (TOP/s) dense
 
 
@@ -49,6 +50,50 @@ def traffic_from_profile(name, launches_bytes_alg):
     return d.get("hbm_bytes_per_launch")
 
 
+def _pmc_values(d, counter, name_part):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc CSV run under d,
+    for kernels whose name contains name_part (case-insensitive)."""
+    import csv
+    import glob
+    vals = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"].lower():
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic_summary(d, calib_bytes):
+    """HBM bytes per launch of the fp16 workload from four PMC runs under d:
+    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of the bench's fp16 launches),
+    calib_fetch/ and calib_write/ (the same counters on --calib-copy, a plain
+    copy of calib_bytes bytes).  Each counter is scaled by what it reads for
+    the copy; the result goes to profiles/traffic_fp16_2k.json with the
+    kernel source hash it was taken on."""
+    def med(v):
+        v = sorted(v[1:] if len(v) > 2 else v)   # the first launch is cold
+        return v[len(v) // 2]
+    fk = _pmc_values(os.path.join(d, "fetch"), "FETCH_SIZE", "gemm_dma_kernel")
+    wk = _pmc_values(os.path.join(d, "write"), "WRITE_SIZE", "gemm_dma_kernel")
+    cf = _pmc_values(os.path.join(d, "calib_fetch"), "FETCH_SIZE", "copy")
+    cw = _pmc_values(os.path.join(d, "calib_write"), "WRITE_SIZE", "copy")
+    if not (fk and wk and cf and cw):
+        sys.exit("traffic: missing PMC values under %s" % d)
+    ff = calib_bytes / (med(cf) * 1024.0)
+    fw = calib_bytes / (med(cw) * 1024.0)
+    fetch_b, write_b = med(fk) * 1024.0 * ff, med(wk) * 1024.0 * fw
+    res = {"kernel_hash": kernel_source_hash(),
+           "hbm_bytes_per_launch": round(fetch_b + write_b),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "fetch_kib_raw": med(fk), "write_kib_raw": med(wk),
+           "copy_scale_fetch": round(ff, 4), "copy_scale_write": round(fw, 4),
+           "dispatches": [len(fk), len(wk), len(cf), len(cw)]}
+    with open(os.path.join(ROOT, "profiles", "traffic_fp16_2k.json"), "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res), flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -60,8 +105,8 @@ def parse():
     p.add_argument("--direction", default="zn")
     p.add_argument("--remap", type=int, default=1)
     p.add_argument("--grid", type=int, default=0)
-    p.add_argument("--mx-tile", default="128x128")
-    p.add_argument("--mx-split", type=int, default=2)
+    p.add_argument("--mx-tile", default="64x128")
+    p.add_argument("--mx-split", type=int, default=1)
     p.add_argument("--no-mx", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
@@ -69,6 +114,8 @@ def parse():
                    help="only run the fp16 workload under every swizzle setting (Zn / Nz offsets "
                         "1, 2, 4, 8 and RASTER, XCD remap off / on) at the 256x128 and the 64x64 "
                         "tile, --steps launches each, for per-setting rocprofv3 counters")
+    p.add_argument("--traffic-from", default="",
+                   help="write profiles/traffic_fp16_2k.json from the PMC runs under this folder")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run plain 256 MiB device copies (the known-size reference that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -131,11 +178,14 @@ def main():
               "(the GEMM would shard by tiles / batches / groups with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        traffic_summary(args.traffic_from, CALIB_BYTES)
+        return
     import numpy as np
     import torch
 
     if args.calib_copy:
-        n = 256 << 20
+        n = CALIB_BYTES
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):

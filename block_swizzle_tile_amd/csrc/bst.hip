@@ -263,8 +263,10 @@ void fill_ws(GemmArgs& a, const Plan& p, void* ws) {
 }
 
 bst_status launch(const Plan& p, const GemmArgs& a, void* stream) {
+  GemmArgs b = a;
+  b.grid = p.grid;
   const hipError_t e =
-      p.inst->launch(dim3(p.grid), dim3(p.inst->threads), (hipStream_t)stream, a);
+      p.inst->launch(dim3(p.grid), dim3(p.inst->threads), (hipStream_t)stream, b);
   if (e != hipSuccess) return fail(BST_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return BST_OK;
 }
@@ -447,6 +449,7 @@ bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const
   a.map_out = out;
   uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, a.tiles)
                                : (uint32_t)std::min<int64_t>(device_cus(), a.tiles);
+  a.grid = grid;
   hipLaunchKernelGGL((tile_map_kernel<false>), dim3(grid), dim3(64), 0, (hipStream_t)stream, a,
                      p.bm, p.bn);
   const hipError_t e = hipGetLastError();
@@ -480,6 +483,7 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
   a.map_out = out;
   uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, (uint32_t)p.tile_cap)
                                : (uint32_t)std::min<int64_t>(device_cus(), p.tile_cap);
+  a.grid = grid;
   hipLaunchKernelGGL((tile_map_kernel<true>), dim3(grid), dim3(64), 0, (hipStream_t)stream, a,
                      p.bm, p.bn);
   const hipError_t e = hipGetLastError();

@@ -67,6 +67,9 @@ struct GemmArgs {
   uint32_t split;                     // K slices per tile (>= 1)
   uint32_t kslice;                    // K elements per slice (multiple of the stage depth)
   uint32_t remap;                     // XCD-contiguous renumbering of workgroups
+  uint32_t grid;                      // workgroups launched (gridDim.x, passed here because the
+                                      // kernel would read it from the dispatch packet in host
+                                      // memory: about a microsecond at every kernel start)
   uint32_t cdtype;                    // OutKind
   float* ws_part;                     // split > 1: [split][tile capacity][BM*BN] partials
   uint32_t* ws_count;                 // split > 1: one arrival counter per tile
@@ -193,13 +196,16 @@ __host__ __device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t
 }
 
 // Workgroup renumbering: hardware places workgroup w on XCD w % 8; with
-// remap on, XCD x gets a contiguous block of logical indices.
-__device__ __forceinline__ uint32_t logical_wg(uint32_t remap) {
-  const uint32_t w = blockIdx.x, G = gridDim.x;
-  if (!remap) return w;
+// remap on, XCD x gets a contiguous block of logical indices.  G: the
+// number of workgroups launched.
+// Branch-free, so that the compiler issues every kernel-argument load of the
+// kernel's start in one batch instead of waiting for `remap` first.
+__device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t G) {
+  const uint32_t w = blockIdx.x;
   const uint32_t x = w % kNumXcd, q = w / kNumXcd;
   const uint32_t base = G / kNumXcd, rem = G % kNumXcd;
-  return x * base + (x < rem ? x : rem) + q;
+  const uint32_t lw = x * base + (x < rem ? x : rem) + q;
+  return remap ? lw : w;
 }
 
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -318,16 +324,18 @@ struct Epilogue {
   // moves 1 KiB of contiguous memory.
   static constexpr int kDeviceScope = 16;  // cache policy bit sc1 on gfx950
 
+  // lead: this wave holds a share of the tile (false for the waves of a
+  // second K group, which only take part in the barriers).
   __device__ __attribute__((always_inline)) static bool fixup(const GemmArgs& a,
                                                               Acc (&acc)[FM][FN], uint32_t s,
-                                                              uint32_t t) {
-    if (a.split <= 1) return true;
+                                                              uint32_t t, bool lead = true) {
+    if (a.split <= 1) return lead;
     __shared__ uint32_t last_flag;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = threadIdx.x & 63u;
     const size_t tile_bytes = (size_t)BM * BN * 4;
     const uint32_t wave_off = wave * FM * FN * 4096u + lane * 16u;
-    {
+    if (lead) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)s * a.tile_cap + t) * tile_bytes,
           (short)0, (int)tile_bytes, 0x00020000);
@@ -357,7 +365,7 @@ struct Epilogue {
       last_flag = (prev == a.split - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (last_flag == 0) return false;
+    if (last_flag == 0 || !lead) return false;
     // Sum in slice order.  A whole slice's partials (two slices' when the
     // wave's part of the tile is small enough to hold twice in registers)
     // are requested before any is added, so the loads overlap instead of
@@ -803,7 +811,7 @@ struct GemmKernel {
     const uint32_t wm = wave / WN, wn = wave % WN;
     const uint32_t lane = threadIdx.x & 63u;
 
-    for (uint32_t u = logical_wg(a.remap); u < units; u += gridDim.x) {
+    for (uint32_t u = logical_wg(a.remap, a.grid); u < units; u += a.grid) {
       const uint32_t s = u / T_tiles;       // K slice (like GetBatchIdx over slices)
       const uint32_t t = u - s * T_tiles;   // task
       const Task tk = decode_task(a, t, BM, BN, gt);
@@ -865,7 +873,7 @@ __global__ void __launch_bounds__(64) tile_map_kernel(GemmArgs a, uint32_t BM, u
     build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
     T_tiles = gtab.first_task[a.G];
   }
-  for (uint32_t t = logical_wg(a.remap); t < T_tiles; t += gridDim.x) {
+  for (uint32_t t = logical_wg(a.remap, a.grid); t < T_tiles; t += a.grid) {
     const Task tk = decode_task(a, t, BM, BN, gt);
     if (threadIdx.x == 0) {
       uint32_t* o = a.map_out + (size_t)t * 8;

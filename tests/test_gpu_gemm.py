@@ -88,7 +88,7 @@ def test_ragged_shapes(orc, M, N, K, kind):
     # bf16 rounding alone is then up to 2^-8 of the result (fp16: 2^-11).
     out_dt = torch.float16 if kind == "f16" else torch.float32
     okind = "f16" if kind == "f16" else "f32"
-    for tile in [(64, 64), (128, 128), (256, 128), (128, 64), (64, 128)]:
+    for tile in [(64, 64), (128, 128), (256, 128), (128, 64), (64, 128), (256, 256)]:
         for split in [1, 3]:
             say("ragged", kind, M, N, K, tile, split)
             Cfull = torch.full((M + 2, ldc), float("nan"), dtype=out_dt, device="cuda")
@@ -192,7 +192,8 @@ def test_mxfp8_workload(orc):
     sa, sb = to_gpu(w["scale_a"], "u8"), to_gpu(w["scale_b"], "u8")
     for sched in [dict(tile=(256, 256), offset=4), dict(tile=(128, 128), offset=2, split_k=2),
                   dict(tile=(256, 128), offset=1, split_k=0, xcd_remap=1),
-                  dict(tile=(128, 64), offset=8, xcd_remap=1)]:
+                  dict(tile=(128, 64), offset=8, xcd_remap=1),
+                  dict(tile=(64, 128), offset=8, xcd_remap=1)]:
         say("mxfp8", sched)
         C = bst().gemm(A, B, scale_a=sa, scale_b=sb, sched=bst().make_sched(**sched))
         check_close(orc, take(C, rows), ref, den, TOL_8, str(sched))
