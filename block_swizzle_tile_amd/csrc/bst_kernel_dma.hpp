@@ -225,7 +225,7 @@ struct DmaKernel {
   static constexpr int LPS = A_IPW + B_IPW + SA_IPW + SB_IPW;  // DMA instructions / wave / stage
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
 
-  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
+  static_assert(STAGES >= 2 && STAGES <= 6, "2..6 stages");
   static_assert((KG == 1 || KG == 2) && KSTEPS % KG == 0, "one or two K groups");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA waves");
   static_assert(SA_BYTES % (256 * NW) == 0 && SB_BYTES % (256 * NW) == 0, "whole scale waves");
@@ -677,16 +677,14 @@ struct DmaKernel {
     LoopTrace tr;
     tr.begin();
     const Dma d = make_dma<FULL>(c);
-    issue<0, FULL>(c, d, c.k0);
-    if constexpr (STAGES > 2) issue<1, FULL>(c, d, c.k0 + BK);
     uint32_t kt = 0;
     if constexpr (STAGES > 2) {
-      if constexpr (STAGES == 4) {
-        issue<2, FULL>(c, d, c.k0 + 2 * BK);
-        wait_vm<2 * LPS>();  // stage 0 resident
-      } else {
-        wait_vm<LPS>();
-      }
+      // stages 0..STAGES-2 in flight, then stage 0 resident
+      static_for<STAGES - 1>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        issue<I, FULL>(c, d, c.k0 + I * BK);
+      });
+      wait_vm<(STAGES - 2) * LPS>();
       barrier_lds();
       KFrag f[NSET];
       static_for<PD>([&](auto g) {
@@ -694,26 +692,25 @@ struct DmaKernel {
         load_kstep<0, GG>(f[GG], wm, wn, kgo_of(c));
       });
       tr.prologue_done();
-      constexpr int WM_ = (STAGES == 4) ? LPS : 0;  // steady-state wait
+      // At the top of step kt the stages up to kt+STAGES-2 have been
+      // issued and kt+1 must be resident: STAGES-3 stages may stay in flight.
+      constexpr int WSTEADY = (STAGES - 3) * LPS;
       for (; kt + UNR < nkp; kt += UNR) {
-        step_ring<0, FULL, true, WM_, false>(acc, f, c, d, kt, wm, wn, tr);
-        step_ring<1, FULL, true, WM_, false>(acc, f, c, d, kt + 1, wm, wn, tr);
-        step_ring<2, FULL, true, WM_, false>(acc, f, c, d, kt + 2, wm, wn, tr);
-        if constexpr (STAGES == 4) step_ring<3, FULL, true, WM_, false>(acc, f, c, d, kt + 3, wm, wn, tr);
+        static_for<UNR>([&](auto i) {
+          constexpr int I = decltype(i)::value;
+          step_ring<I, FULL, true, WSTEADY, false>(acc, f, c, d, kt + I, wm, wn, tr);
+        });
       }
-      // last group: only its first step has a stage left to issue, and the
-      // last step waits for nothing
-      if constexpr (STAGES == 4) {
-        step_ring<0, FULL, true, LPS, false>(acc, f, c, d, kt, wm, wn, tr);
-        step_ring<1, FULL, false, LPS, false>(acc, f, c, d, kt + 1, wm, wn, tr);
-        step_ring<2, FULL, false, 0, false>(acc, f, c, d, kt + 2, wm, wn, tr);
-        step_ring<3, FULL, false, -1, true>(acc, f, c, d, kt + 3, wm, wn, tr);
-      } else {
-        step_ring<0, FULL, true, 0, false>(acc, f, c, d, kt, wm, wn, tr);
-        step_ring<1, FULL, false, 0, false>(acc, f, c, d, kt + 1, wm, wn, tr);
-        step_ring<2, FULL, false, -1, true>(acc, f, c, d, kt + 2, wm, wn, tr);
-      }
+      // Last group: only its first step has a stage left to issue (the
+      // last one), so from its second step on STAGES-2-I stages remain in
+      // flight, and the last step waits for nothing.
+      static_for<UNR>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        constexpr int W = (I == UNR - 1) ? -1 : (I == 0 ? WSTEADY : (STAGES - 2 - I) * LPS);
+        step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr);
+      });
     } else {
+      issue<0, FULL>(c, d, c.k0);
       tr.prologue_done();
       for (; kt + STAGES < nkp; kt += STAGES) {
         step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);

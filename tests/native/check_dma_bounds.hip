@@ -279,6 +279,9 @@ int main() {
   run_plain<AB_F16, 128, 64, 4, 2, 4>(p16);
   run_plain<AB_F16, 64, 128, 2, 4, 4>(p16);
   run_plain<AB_F16, 256, 256, 4, 2, 2>(p16);
+  run_plain<AB_F16, 64, 64, 2, 2, 6>(p16);
+  run_plain<AB_F16, 64, 64, 2, 2, 6, 2>(p16);
+  run_plain<AB_F16, 64, 64, 2, 2, 5>(p16);
   run_plain<AB_F16, 64, 64, 2, 2, 4, 2>(p16);
   run_plain<AB_F16, 128, 64, 2, 2, 4, 2>(p16);
   run_plain<AB_F16, 64, 128, 2, 2, 4, 2>(p16);
@@ -317,6 +320,9 @@ int main() {
   run_plain<AB_MXE4M3, 128, 64, 4, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 4, 4>(pmx);
   run_plain<AB_MXE4M3, 64, 64, 2, 2, 4, 2>(pmx);
+  run_plain<AB_MXE4M3, 64, 128, 2, 2, 6>(pmx);
+  run_plain<AB_MXE4M3, 128, 64, 2, 2, 6>(pmx);
+  run_plain<AB_MXE4M3, 64, 128, 2, 2, 5>(pmx);
   run_plain<AB_MXE4M3, 128, 64, 2, 2, 4, 2>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 2, 4, 2>(pmx);
   run_plain<AB_MXE4M3, 128, 128, 2, 2, 4, 2>(pmx);
