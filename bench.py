@@ -114,6 +114,8 @@ def parse():
                    help="only run the fp16 workload under every swizzle setting (Zn / Nz offsets "
                         "1, 2, 4, 8 and RASTER, XCD remap off / on) at the 256x128 and the 64x64 "
                         "tile, --steps launches each, for per-setting rocprofv3 counters")
+    p.add_argument("--all-configs", action="store_true",
+                   help="time every workload configuration (one JSON line per schedule)")
     p.add_argument("--traffic-from", default="",
                    help="write profiles/traffic_fp16_2k.json from the PMC runs under this folder")
     p.add_argument("--calib-copy", action="store_true",
@@ -171,6 +173,76 @@ def l2_sweep(args, bst, I, gpu, torch):
         torch.cuda.synchronize()
 
 
+def all_configs(args, bst, I, gpu, torch):
+    """Every configuration of the workload set, at its stated tile and at the
+    faster schedules, timed like the headline (warm, graph replay of
+    args.steps launches); one JSON line per (config, schedule)."""
+    out = []
+
+    def run(name, flop, dtype, sched_kw, fn):
+        s = bst.make_sched(**sched_kw)
+        tot, per = time_launches(lambda: fn(s), args.steps, args.warmup)
+        tf = flop / (per * 1e-3) / 1e12
+        rec = {"config": name, "sched": {k: list(v) if isinstance(v, tuple) else v
+                                         for k, v in sched_kw.items()},
+               "us_per_launch": round(per * 1e3, 3), "tflops": round(tf, 2),
+               "pct_of_peak": round(100.0 * tf / PEAK[dtype], 2)}
+        out.append(rec)
+        print(json.dumps(rec), flush=True)
+
+    w = I.workload("tails")
+    A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    f1 = 2.0 * w["M"] * w["N"] * w["K"]
+    run("C1 fp16 200x136x256", f1, "f16", dict(tile=(64, 64), offset=3, direction="zn"),
+        lambda s: bst.gemm(A, B, C, sched=s))
+
+    w = I.workload("fp16_2k")
+    A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    f2 = 2.0 * w["M"] * w["N"] * w["K"]
+    for kw in (dict(tile=(256, 128), offset=1, direction="zn", xcd_remap=1),
+               dict(tile=(256, 128), offset=4, direction="zn", xcd_remap=0),
+               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1)):
+        run("C2 fp16 1024x1024x2048", f2, "f16", kw, lambda s: bst.gemm(A, B, C, sched=s))
+
+    x = I.workload("mxfp8_4k")
+    Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
+    sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
+    Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
+    f3 = 2.0 * x["M"] * x["N"] * x["K"]
+    for kw in (dict(tile=(256, 256), offset=4, direction="zn", xcd_remap=0),
+               dict(tile=(256, 256), offset=4, direction="zn", xcd_remap=1),
+               dict(tile=(64, 128), offset=8, direction="zn", xcd_remap=1)):
+        run("C3 MX-fp8 1024x2048x4096", f3, "e4m3", kw,
+            lambda s: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s))
+
+    b = I.workload("bf16_batch")
+    Ab, Bb = gpu(b["A"], "bf16"), gpu(b["B"], "bf16")
+    Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
+    f4 = 2.0 * b["batch"] * b["M"] * b["N"] * b["K"]
+    for kw in (dict(tile=(128, 192), offset=1, direction="zn"),
+               dict(tile=(128, 192), offset=1, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1),
+               dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1)):
+        run("C4 bf16 16x512x768x1024", f4, "bf16", kw, lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s))
+
+    g = I.workload("int8_groups")
+    Ag, Bg = gpu(g["A"], "i8"), gpu(g["B"], "i8")
+    gm = gpu(g["group_m"], "i32")
+    rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
+    Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
+    f5 = 2.0 * g["total_m"] * g["N"] * g["K"]
+    for kw in (dict(tile=(256, 256), offset=1, direction="zn"),
+               dict(tile=(256, 256), offset=1, direction="zn", xcd_remap=1),
+               dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)):
+        run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8", kw,
+            lambda s: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs,
+                                                sched=s))
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -203,8 +275,13 @@ def main():
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
         if kind == "e4m3":
             return torch.from_numpy(a.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
+        if kind == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
 
+    if args.all_configs:
+        all_configs(args, bst, I, gpu, torch)
+        return
     if args.l2_sweep:
         l2_sweep(args, bst, I, gpu, torch)
         return
