@@ -324,18 +324,16 @@ struct Epilogue {
   // moves 1 KiB of contiguous memory.
   static constexpr int kDeviceScope = 16;  // cache policy bit sc1 on gfx950
 
-  // lead: this wave holds a share of the tile (false for the waves of a
-  // second K group, which only take part in the barriers).
   __device__ __attribute__((always_inline)) static bool fixup(const GemmArgs& a,
                                                               Acc (&acc)[FM][FN], uint32_t s,
-                                                              uint32_t t, bool lead = true) {
-    if (a.split <= 1) return lead;
+                                                              uint32_t t) {
+    if (a.split <= 1) return true;
     __shared__ uint32_t last_flag;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = threadIdx.x & 63u;
     const size_t tile_bytes = (size_t)BM * BN * 4;
     const uint32_t wave_off = wave * FM * FN * 4096u + lane * 16u;
-    if (lead) {
+    {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           reinterpret_cast<uint8_t*>(a.ws_part) + ((size_t)s * a.tile_cap + t) * tile_bytes,
           (short)0, (int)tile_bytes, 0x00020000);
@@ -365,7 +363,7 @@ struct Epilogue {
       last_flag = (prev == a.split - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (last_flag == 0 || !lead) return false;
+    if (last_flag == 0) return false;
     // Sum in slice order.  A whole slice's partials (two slices' when the
     // wave's part of the tile is small enough to hold twice in registers)
     // are requested before any is added, so the loads overlap instead of

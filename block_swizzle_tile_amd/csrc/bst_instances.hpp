@@ -35,9 +35,9 @@ hipError_t launch_reg(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
   return hipGetLastError();
 }
 
-template <int AB, int BM, int BN, int WM, int WN, int S, bool GR, int KG>
+template <int AB, int BM, int BN, int WM, int WN, int S, bool GR>
 hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
-  hipLaunchKernelGGL((gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR, KG>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -47,13 +47,11 @@ hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
         reinterpret_cast<const void*>(&gemm_kernel<AB, BM, BN, WM, WN, GR>),              \
         &launch_reg<AB, BM, BN, WM, WN, GR>, 64 * WM * WN, Traits<AB>::BK                 \
   }
-#define BST_DMA(AB, BM, BN, WM, WN, S, GR) BST_DMA_KG(AB, BM, BN, WM, WN, S, GR, 1)
-// KG = 2: two K groups of WM x WN waves (see DmaKernel)
-#define BST_DMA_KG(AB, BM, BN, WM, WN, S, GR, KG)                                         \
+#define BST_DMA(AB, BM, BN, WM, WN, S, GR)                                                \
   Instance {                                                                              \
     AB, BM, BN, GR, true, S,                                                              \
-        reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR, KG>),   \
-        &launch_dma<AB, BM, BN, WM, WN, S, GR, KG>, 64 * WM * WN * KG, Traits<AB>::BK     \
+        reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR>),       \
+        &launch_dma<AB, BM, BN, WM, WN, S, GR>, 64 * WM * WN, Traits<AB>::BK              \
   }
 
 InstanceList instances_f16();

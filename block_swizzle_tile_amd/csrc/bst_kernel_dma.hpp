@@ -188,25 +188,16 @@ struct LoopTrace {
 // chunk blocks inside which a B row is permuted.
 constexpr int pow2_block(int n) { return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1; }
 
-// KG K groups: the workgroup holds KG copies of the WM x WN wave layout,
-// and group g runs the MFMAs of K steps [g*KSG, (g+1)*KSG) of every stage
-// (KSG = K steps per stage / KG), while all KG*WM*WN waves share the
-// stage's DMA.  A wave issues a bounded rate of vector-memory and LDS
-// instructions whatever the CU's headroom, so two groups double the rate at
-// which a small tile's stages are fetched and read, at the cost of one
-// accumulator exchange through LDS per task.
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, int KG = 1>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
 struct DmaKernel {
   using T = Traits<AB>;
   using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
   using Acc = typename Epi::Acc;
   using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
-  static constexpr int NWC = WM * WN;  // waves of one K group
-  static constexpr int NW = NWC * KG, NT = 64 * NW;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   static constexpr int ES = T::ES, BK = T::BK, CE = 16 / ES;
   static constexpr int KSTEPS = BK / T::MFMA_K;
-  static constexpr int KSG = KSTEPS / KG;  // K steps of a stage per K group
   static constexpr int RB = BN * ES;     // bytes of one B row (one K index) in LDS
   static constexpr int NCH = RB / 16;    // 16-byte chunks per B row
   static constexpr uint32_t BSWZ = pow2_block(NCH) - 1;
@@ -226,7 +217,6 @@ struct DmaKernel {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
 
   static_assert(STAGES >= 2 && STAGES <= 6, "2..6 stages");
-  static_assert((KG == 1 || KG == 2) && KSTEPS % KG == 0, "one or two K groups");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA waves");
   static_assert(SA_BYTES % (256 * NW) == 0 && SB_BYTES % (256 * NW) == 0, "whole scale waves");
   static_assert(LPS * STAGES < 64, "vmcnt holds 6 bits");
@@ -265,7 +255,6 @@ struct DmaKernel {
     uint32_t k0;             // first K index of the task's slice
     uint32_t kend;
     uint32_t wave;
-    uint32_t kgo;            // first K step (inside a stage) of the wave's K group
     Lanes ln;
   };
 
@@ -446,9 +435,8 @@ struct DmaKernel {
 
   // LDS -> registers, one operand fragment at a time: A fragment I and B
   // fragment J of K step KK of stage buffer S, with their block scales.
-  template <int S, int KL, int I>
-  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, uint32_t kgo) {
-    const uint32_t KK = KL + kgo;  // K step inside the stage
+  template <int S, int KK, int I>
+  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
     const lds_t* lsa = base + A_BYTES + B_BYTES;
@@ -470,9 +458,8 @@ struct DmaKernel {
       f.sa[I] = 0x7fu;  // 2^0 (the scale operand only matters to fp8 MFMAs)
   }
 
-  template <int S, int KL, int J>
-  __device__ static __forceinline__ void load_b(KFrag& f, uint32_t wn, uint32_t kgo) {
-    const uint32_t KK = KL + kgo;  // K step inside the stage
+  template <int S, int KK, int J>
+  __device__ static __forceinline__ void load_b(KFrag& f, uint32_t wn) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* lb = base + A_BYTES;
     const lds_t* lsb = base + A_BYTES + B_BYTES + SA_BYTES;
@@ -516,30 +503,21 @@ struct DmaKernel {
       f.sb[J] = 0x7fu;
   }
 
-  // Fragment load X of the group's K step KL: A fragments 0..FM-1, then B
-  // fragments 0..FN-1.
-  static constexpr int NLK = FM + FN;     // fragment loads per K step
-  static constexpr int NMK = FM * FN;     // MFMAs per K step
-  static constexpr int NMF = KSG * NMK;   // MFMAs per stage and wave
+  // Fragment load X of K step KK: A fragments 0..FM-1, then B fragments 0..FN-1.
+  static constexpr int NLK = FM + FN;       // fragment loads per K step
+  static constexpr int NMK = FM * FN;       // MFMAs per K step
+  static constexpr int NMF = KSTEPS * NMK;  // MFMAs per stage
 
-  template <int S, int KL, int X>
-  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn,
-                                                  uint32_t kgo) {
+  template <int S, int KK, int X>
+  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn) {
     if constexpr (X < FM)
-      load_a<S, KL, X>(f, wm, kgo);
+      load_a<S, KK, X>(f, wm);
     else
-      load_b<S, KL, X - FM>(f, wn, kgo);
+      load_b<S, KK, X - FM>(f, wn);
   }
-  template <int S, int KL>
-  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn,
-                                                    uint32_t kgo) {
-    static_for<NLK>([&](auto x) { load_one<S, KL, decltype(x)::value>(f, wm, wn, kgo); });
-  }
-  __device__ static __forceinline__ uint32_t kgo_of(const Ctx& c) {
-    if constexpr (KG == 1)
-      return 0u;
-    else
-      return c.kgo;
+  template <int S, int KK>
+  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn) {
+    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value>(f, wm, wn); });
   }
 
   // MFMA Q of a K step (A fragment major).
@@ -584,18 +562,18 @@ struct DmaKernel {
   // the reads run inside the stage only: the MFMAs of K step kk carry the
   // reads of K step kk+1.
   static constexpr int UNR = STAGES;  // steps per loop trip: buffer index stays compile-time
-  static constexpr int RING_K = UNR * KSG;  // the group's K steps per loop trip
+  static constexpr int RING_K = UNR * KSTEPS;  // K steps per loop trip
   // The ring's read-ahead: as far as 3 K steps (and never past the next
   // stage), with a set count that divides the K steps of one trip so that
   // every set index is a compile-time constant.
   static constexpr int ring_pd() {
-    for (int dd = (KSG < 3 ? KSG : 3); dd > 1; --dd)
+    for (int dd = (KSTEPS < 3 ? KSTEPS : 3); dd > 1; --dd)
       if (RING_K % (dd + 1) == 0) return dd;
     return 1;
   }
   static constexpr int PD = ring_pd();
   static constexpr int NSET = PD + 1;
-  static_assert(STAGES == 2 || (RING_K % NSET == 0 && PD <= KSG), "ring shape");
+  static_assert(STAGES == 2 || (RING_K % NSET == 0 && PD <= KSTEPS), "ring shape");
 
   __host__ __device__ __forceinline__ static uint32_t padded_stages(uint32_t nk) {
     return (nk + UNR - 1) / UNR * UNR;
@@ -624,18 +602,17 @@ struct DmaKernel {
     }
     tr.released();
     const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
-    const uint32_t kgo = kgo_of(c);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
-      constexpr int G = I * KSG + KK;  // the group's K step inside the trip
+      constexpr int G = I * KSTEPS + KK;  // K step inside the trip
       mfma_one<R>(acc, f[G % NSET]);
       if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
       constexpr int GL = G + PD;  // the K step whose operands are read now
       if constexpr (!(LAST && GL >= RING_K)) {
-        constexpr int SB = (GL / KSG) % STAGES, KL = GL % KSG;
+        constexpr int SB = (GL / KSTEPS) % STAGES, KL = GL % KSTEPS;
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn, kgo);
+          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -653,17 +630,16 @@ struct DmaKernel {
     barrier_lds();
     tr.released();
     const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
-    const uint32_t kgo = kgo_of(c);
     KFrag g0, g1;
-    load_kstep<S, 0>(g0, wm, wn, kgo);
+    load_kstep<S, 0>(g0, wm, wn);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
       mfma_one<R>(acc, (KK & 1) ? g1 : g0);
       if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
-      if constexpr (KK + 1 < KSG) {
+      if constexpr (KK + 1 < KSTEPS) {
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn, kgo);
+          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -689,7 +665,7 @@ struct DmaKernel {
       KFrag f[NSET];
       static_for<PD>([&](auto g) {
         constexpr int GG = decltype(g)::value;
-        load_kstep<0, GG>(f[GG], wm, wn, kgo_of(c));
+        load_kstep<0, GG>(f[GG], wm, wn);
       });
       tr.prologue_done();
       // At the top of step kt the stages up to kt+STAGES-2 have been
@@ -727,62 +703,6 @@ struct DmaKernel {
     tr.finish(trace_out);
   }
 
-  // K groups: each group's accumulators cover the whole wave tile over its
-  // own K steps.  Every wave stores its accumulators in the (idle) stage
-  // buffers and adds those of the same wave of the other group, so both
-  // groups end with the full sum (the same one: the addition commutes) and
-  // no accumulator passes through a branch.  Slot (piece P, group g) holds
-  // wave tile piece P of group g: [wave][quarter][lane][4 values].
-  static constexpr int XPIECE = NWC * 4096;
-  static constexpr int XPB = STAGE_BYTES / XPIECE;  // slots per stage buffer
-  static_assert(KG == 1 || (XPB >= 1 && FM * FN * KG <= XPB * STAGES),
-                "the accumulator exchange fits in the stage buffers");
-  template <int SLOT>
-  __device__ static __forceinline__ lds_t* xslot() {
-    return stage_buf<SLOT % STAGES, STAGE_BYTES>() + (SLOT / STAGES) * XPIECE;
-  }
-  __device__ static __forceinline__ void exchange(Acc (&acc)[FM][FN], uint32_t wave) {
-    const uint32_t kg = wave / NWC;
-    const uint32_t off = (wave % NWC) * 4096u + (threadIdx.x & 63u) * 16u;
-    static_for<FM * FN>([&](auto p) {
-      constexpr int P = decltype(p)::value, I = P / FN, J = P % FN;
-      lds_t* mine = kg == 0 ? xslot<P * KG>() : xslot<P * KG + 1>();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const auto x = acc[I][J][4 * q + e];
-          v[e] = __builtin_bit_cast(uint32_t, x);
-        }
-        *(lds_u32x4_t*)(mine + off + q * 1024u) = v;
-      }
-    });
-    wait_lgkm0();  // the stores have reached LDS before the other group reads them
-    barrier_lds();
-    static_for<FM * FN>([&](auto p) {
-      constexpr int P = decltype(p)::value, I = P / FN, J = P % FN;
-      const lds_t* other = kg == 0 ? xslot<P * KG + 1>() : xslot<P * KG>();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t v = *(const lds_u32x4_t*)(other + off + q * 1024u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // copy the element out first: a bit_cast of a vector-element
-          // expression would read element 0
-          const uint32_t x = v[e];
-          if constexpr (T::IS_INT)
-            acc[I][J][4 * q + e] += __builtin_bit_cast(int, x);
-          else
-            acc[I][J][4 * q + e] += __builtin_bit_cast(float, x);
-        }
-      }
-    });
-    // the next task's prologue refills the stage buffers
-    wait_lgkm0();
-    barrier_lds();
-  }
-
   // One task: K loop (if any), split-K fix-up, epilogue.
   template <bool FULL>
   __device__ static __forceinline__ void task(const GemmArgs& a, const Ctx& c, const Task& tk,
@@ -797,12 +717,9 @@ struct DmaKernel {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
     if (nk > 0) kloop<FULL>(acc, c, padded_stages(nk), wm, wn, a.trace);
-    if constexpr (KG > 1) exchange(acc, c.wave);
     const uint64_t t_epi = trace_stamp();
     uint64_t t_fix = t_epi;
-    // group 0 writes the tile (both groups take part in the fix-up's barriers)
-    const bool lead = KG == 1 || c.wave < NWC;
-    if (Epi::fixup(a, acc, s, t, lead)) {
+    if (Epi::fixup(a, acc, s, t)) {
       t_fix = trace_stamp();
       Epi::store_tile(a, tk, acc, wm, wn);
     }
@@ -845,8 +762,7 @@ struct DmaKernel {
     c.ldsb = a.ldsb;
     c.ldb_bytes32 = (uint32_t)c.ldb_bytes;
     c.ldsb32 = (uint32_t)a.ldsb;
-    const uint32_t wm = (c.wave % NWC) / WN, wn = (c.wave % NWC) % WN;
-    c.kgo = (c.wave / NWC) * KSG;
+    const uint32_t wm = c.wave / WN, wn = c.wave % WN;
 
     // The host launches at most one workgroup per unit, so a plain launch's
     // first unit exists and the loop needs no test before it (which lets the
@@ -893,10 +809,10 @@ struct DmaKernel {
   }
 };
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, int KG = 1>
-__global__ void __launch_bounds__(64 * WM * WN * KG) gemm_dma_kernel(GemmArgs a) {
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only builtins: device pass only
-  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED, KG>::run(a);
+  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>::run(a);
 #endif
 }
 

@@ -44,9 +44,9 @@ struct Problem {
   bool scaled = false;
 };
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, int KG = 1>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
 void check(const Problem& p) {
-  using KN = DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED, KG>;
+  using KN = DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>;
   constexpr int ES = KN::ES, BK = KN::BK, CE = KN::CE, NW = KN::NW;
   // schedule: the same split resolution as the host planner (no empty slices)
   const int64_t nk_all = (p.K + BK - 1) / BK;
@@ -250,9 +250,9 @@ static Problem grouped(const char* n, std::vector<int32_t> g, int64_t spare, int
   return p;
 }
 
-template <int AB, int BM, int BN, int WM, int WN, int S, int KG = 1>
+template <int AB, int BM, int BN, int WM, int WN, int S>
 void run_plain(const std::vector<Problem>& ps) {
-  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, false, KG>(p);
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, false>(p);
 }
 template <int AB, int BM, int BN, int WM, int WN, int S>
 void run_grouped(const std::vector<Problem>& ps) {
@@ -280,12 +280,7 @@ int main() {
   run_plain<AB_F16, 64, 128, 2, 4, 4>(p16);
   run_plain<AB_F16, 256, 256, 4, 2, 2>(p16);
   run_plain<AB_F16, 64, 64, 2, 2, 6>(p16);
-  run_plain<AB_F16, 64, 64, 2, 2, 6, 2>(p16);
   run_plain<AB_F16, 64, 64, 2, 2, 5>(p16);
-  run_plain<AB_F16, 64, 64, 2, 2, 4, 2>(p16);
-  run_plain<AB_F16, 128, 64, 2, 2, 4, 2>(p16);
-  run_plain<AB_F16, 64, 128, 2, 2, 4, 2>(p16);
-  run_plain<AB_F16, 128, 128, 2, 2, 4, 2>(p16);
   run_grouped<AB_F16, 128, 128, 2, 2, 4>(g16);
   // 8-bit operands: K and N multiples of 16
   const std::vector<Problem> p8 = {
@@ -319,13 +314,9 @@ int main() {
   run_plain<AB_MXE4M3, 64, 128, 2, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 128, 64, 4, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 4, 4>(pmx);
-  run_plain<AB_MXE4M3, 64, 64, 2, 2, 4, 2>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 2, 6>(pmx);
   run_plain<AB_MXE4M3, 128, 64, 2, 2, 6>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 2, 5>(pmx);
-  run_plain<AB_MXE4M3, 128, 64, 2, 2, 4, 2>(pmx);
-  run_plain<AB_MXE4M3, 64, 128, 2, 2, 4, 2>(pmx);
-  run_plain<AB_MXE4M3, 128, 128, 2, 2, 4, 2>(pmx);
   run_plain<AB_E4M3, 128, 64, 2, 2, 4>(p8);
   run_plain<AB_E4M3, 64, 128, 2, 2, 4>(p8);
   run_plain<AB_MXE4M3, 128, 128, 2, 2, 4>(pmx);
