@@ -453,16 +453,42 @@ struct Epilogue {
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
     uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
                             (int64_t)tk.n * BN) * OS;
+    // Dequant scales are gathered before the first store when they fit in a
+    // few registers: a store counts in vmcnt too, so a scale load issued
+    // after one waits for it (the compiler cannot hoist the loads itself,
+    // since C may alias the scales).  Wide wave tiles load them in place.
+    constexpr bool PRE = DEQ && FN * 16 + FM <= 40;
+    float rsv[FM];
+    float csv[FN][4][4];
     const float* csb = nullptr;
     if constexpr (DEQ)
       csb = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + (int64_t)tk.n * BN;
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t ml = wm * TM + i * 32 + l32;
+        rsv[i] = (FULL || ml < tk.rows_valid) ? a.row_scale[tk.row0 + ml] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            csv[j][g][r] = (FULL || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const uint32_t ml = wm * TM + i * 32 + l32;
       if (!FULL && ml >= tk.rows_valid) continue;
       uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
       float rs = 1.0f;
-      if constexpr (DEQ) rs = a.row_scale[tk.row0 + ml];
+      if constexpr (PRE)
+        rs = rsv[i];
+      else if constexpr (DEQ)
+        rs = a.row_scale[tk.row0 + ml];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -483,7 +509,10 @@ struct Epilogue {
               iv[r] = 0;
             }
           }
-          if constexpr (DEQ) {
+          if constexpr (PRE) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = (f[r] * rs) * csv[j][g][r];
+          } else if constexpr (DEQ) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float c = (whole || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
