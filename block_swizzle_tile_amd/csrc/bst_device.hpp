@@ -44,6 +44,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_out_t;
 
 // ------------------------------------------------------------ arguments ---
 struct GemmArgs {
@@ -444,11 +446,23 @@ struct Epilogue {
   // per-row and per-column scales, out = (float(acc) * row) * column.  FULL:
   // every row and column of the tile is inside the problem, so each lane
   // writes its 4 consecutive values with one vector store and no mask.
-  template <int OUT, bool DEQ, bool FULL>
+  //
+  // SB > 0: `stage` is SB bytes of LDS the workgroup no longer needs.  A
+  // whole tile that fits (rows padded by 16 bytes) goes through it: the
+  // waves write their values row-major into LDS, then every thread stores
+  // consecutive 16-byte chunks, so a store instruction writes whole cache
+  // lines instead of 16 bytes in each of 32 rows (those partial lines stay
+  // dirty in L2 and cost their write-back when the kernel ends).  All waves
+  // of the workgroup call this together (it has barriers).
+  template <int OUT, bool DEQ, bool FULL, int SB>
   __device__ static __forceinline__ void store_as(const GemmArgs& a, const Task& tk,
                                                   const Acc (&acc)[FM][FN], uint32_t wm,
-                                                  uint32_t wn) {
+                                                  uint32_t wn, lds_byte_t* stage) {
     constexpr int OS = (OUT == OUT_F16 || OUT == OUT_BF16) ? 2 : 4;
+    constexpr int PITCH = BN * OS + 16;
+    constexpr int NTH = 64 * WM * WN;
+    constexpr int CPR = BN * OS / 16;  // 16-byte chunks per row
+    constexpr bool STAGED = FULL && SB > 0 && BM * PITCH <= SB && (BM * CPR) % NTH == 0;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
     uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
@@ -520,7 +534,17 @@ struct Epilogue {
             }
           }
           uint8_t* p = crow + nl * OS;
-          if (whole) {
+          if constexpr (STAGED) {
+            lds_byte_t* q = stage + ml * PITCH + nl * OS;
+            if constexpr (OS == 2)
+              *(__attribute__((address_space(3))) u32x2_t*)q =
+                  u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
+            else if constexpr (OUT == OUT_F32)
+              *(__attribute__((address_space(3))) f32x4_t*)q = f32x4_t{f[0], f[1], f[2], f[3]};
+            else
+              *(__attribute__((address_space(3))) i32x4_t*)q = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+            (void)p;
+          } else if (whole) {
             if constexpr (OS == 2)
               *(u32x2_t*)__builtin_assume_aligned(p, 8) =
                   u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
@@ -542,42 +566,56 @@ struct Epilogue {
           }
         }
     }
+    if constexpr (STAGED) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < BM * CPR / NTH; ++i) {
+        const uint32_t q = threadIdx.x + (uint32_t)i * NTH;
+        const uint32_t row = q / CPR, c = q % CPR;
+        const u32x4_t v = *(const lds_u32x4_out_t*)(stage + row * PITCH + c * 16);
+        *(u32x4_t*)__builtin_assume_aligned(cbase + (int64_t)row * a.ldc * OS + c * 16, 16) = v;
+      }
+      // the next task's prologue refills the stage buffers
+      __syncthreads();
+    }
   }
 
-  template <bool DEQ, bool FULL>
+  template <bool DEQ, bool FULL, int SB>
   __device__ static __forceinline__ void store_kind(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
-                                                    uint32_t wn) {
+                                                    uint32_t wn, lds_byte_t* stage) {
     if (a.cdtype == OUT_F16)
-      store_as<OUT_F16, DEQ, FULL>(a, tk, acc, wm, wn);
+      store_as<OUT_F16, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
     else if (a.cdtype == OUT_BF16)
-      store_as<OUT_BF16, DEQ, FULL>(a, tk, acc, wm, wn);
+      store_as<OUT_BF16, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
     else if (a.cdtype == OUT_F32)
-      store_as<OUT_F32, DEQ, FULL>(a, tk, acc, wm, wn);
+      store_as<OUT_F32, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
     else if constexpr (T::IS_INT && !DEQ)
-      store_as<OUT_I32, false, FULL>(a, tk, acc, wm, wn);
+      store_as<OUT_I32, false, FULL, SB>(a, tk, acc, wm, wn, stage);
   }
 
   // The wave's whole output: one dispatch per task on the output kind, the
   // dequant and whether the tile is whole, then straight-line stores.
-  // Dequantised outputs exist for int8 operands only.
+  // Dequantised outputs exist for int8 operands only.  SB, stage: LDS that
+  // whole tiles may be staged through (see store_as; SB = 0: none).
+  template <int SB = 0>
   __device__ static __forceinline__ void store_tile(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
-                                                    uint32_t wn) {
+                                                    uint32_t wn, lds_byte_t* stage = nullptr) {
     const bool full = tk.rows_valid >= (uint32_t)BM && tk.nAct >= (uint32_t)BN;
     if constexpr (T::IS_INT) {
       if (a.row_scale != nullptr) {
         if (full)
-          store_kind<true, true>(a, tk, acc, wm, wn);
+          store_kind<true, true, SB>(a, tk, acc, wm, wn, stage);
         else
-          store_kind<true, false>(a, tk, acc, wm, wn);
+          store_kind<true, false, SB>(a, tk, acc, wm, wn, stage);
         return;
       }
     }
     if (full)
-      store_kind<false, true>(a, tk, acc, wm, wn);
+      store_kind<false, true, SB>(a, tk, acc, wm, wn, stage);
     else
-      store_kind<false, false>(a, tk, acc, wm, wn);
+      store_kind<false, false, SB>(a, tk, acc, wm, wn, stage);
   }
 
 };

@@ -721,7 +721,7 @@ struct DmaKernel {
     uint64_t t_fix = t_epi;
     if (Epi::fixup(a, acc, s, t)) {
       t_fix = trace_stamp();
-      Epi::store_tile(a, tk, acc, wm, wn);
+      Epi::template store_tile<STAGE_BYTES>(a, tk, acc, wm, wn, stage_buf<0, STAGE_BYTES>());
     }
 #ifdef BST_TRACE
     const uint64_t t_end = trace_stamp();
