@@ -205,20 +205,26 @@ struct DmaKernel {
   static constexpr int B_BYTES = BK * RB;
   static constexpr int A_IPW = A_BYTES / 1024 / NW;  // 1 KiB DMA instructions per wave
   static constexpr int B_IPW = B_BYTES / 1024 / NW;
-  // MX scales: A as [rows][4 bytes] (one dword = the stage's 4 K blocks of a
-  // row), B as [4][BN] bytes; dword DMA, 256 bytes per instruction, padded so
-  // that every wave issues the same number of instructions.
-  static constexpr int SA_ROWS = T::SCALED ? (BM > 64 * NW ? BM : 64 * NW) : 0;
-  static constexpr int SA_BYTES = SA_ROWS * 4;
-  static constexpr int SB_BYTES = T::SCALED ? (4 * BN > 256 * NW ? 4 * BN : 256 * NW) : 0;
-  static constexpr int SA_IPW = SA_BYTES / 256 / NW;
-  static constexpr int SB_IPW = SB_BYTES / 256 / NW;
-  static constexpr int LPS = A_IPW + B_IPW + SA_IPW + SB_IPW;  // DMA instructions / wave / stage
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  // MX scales: A as [BM rows][4 bytes] (one dword = the stage's 4 K blocks
+  // of a row), B as [4][BN] bytes; dword DMA, 256 bytes per instruction:
+  // SA_N instructions for A (64 rows each) and SB_N for B.  They are dealt
+  // out as slots, SC_IPW per wave (wave w takes slots w*SC_IPW + i), so a
+  // wave issues at most one more than its share; a slot past SA_N + SB_N
+  // issues an all-out-of-range instruction (it writes zeros) into the
+  // stage's 256-byte dummy area, so that every wave issues the same count
+  // for the vmcnt arithmetic.
+  static constexpr int SA_N = T::SCALED ? BM / 64 : 0;
+  static constexpr int SB_N = T::SCALED ? BN / 64 : 0;
+  static constexpr int SC_IPW = (SA_N + SB_N + NW - 1) / NW;
+  static constexpr int SA_BYTES = SA_N * 256;
+  static constexpr int SB_BYTES = SB_N * 256;
+  static constexpr int SD_BYTES = SC_IPW * NW > SA_N + SB_N ? 256 : 0;
+  static constexpr int LPS = A_IPW + B_IPW + SC_IPW;  // DMA instructions / wave / stage
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SD_BYTES;
 
   static_assert(STAGES >= 2 && STAGES <= 6, "2..6 stages");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA waves");
-  static_assert(SA_BYTES % (256 * NW) == 0 && SB_BYTES % (256 * NW) == 0, "whole scale waves");
+  static_assert(!T::SCALED || (BM % 64 == 0 && BN % 64 == 0), "whole 256-byte scale instructions");
   static_assert(LPS * STAGES < 64, "vmcnt holds 6 bits");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 MFMA sub-tiles");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024 - (GROUPED ? (int)sizeof(GroupTable) : 0) - 16,
@@ -239,10 +245,8 @@ struct DmaKernel {
     uint32_t b_off[B_IPW];   // byte offset inside one stage of the B panel
     uint32_t b_k[B_IPW];     // K row inside the stage
     uint32_t b_ok;           // bit i: the chunk's columns are inside N
-    uint32_t sa_off[SA_IPW > 0 ? SA_IPW : 1];
-    uint32_t sa_ok;
-    uint32_t sb_off[SB_IPW > 0 ? SB_IPW : 1];
-    uint32_t sb_ok;
+    uint32_t sc_off[SC_IPW > 0 ? SC_IPW : 1];  // scale slots (see sc_slot)
+    uint32_t sc_ok;
   };
 
   struct Ctx {
@@ -290,19 +294,19 @@ struct DmaKernel {
       ln.b_k[i] = k;
       if (n_tile * BN + ch * CE < N) ln.b_ok |= 1u << i;
     }
-    ln.sa_ok = 0;
-    ln.sb_ok = 0;
-    if constexpr (T::SCALED) {
-      for (int i = 0; i < SA_IPW; ++i) {
-        const uint32_t r = (wave * SA_IPW + i) * 64 + lane;
-        ln.sa_off[i] = (uint32_t)((int64_t)r * ldsa);
-        if (r < (uint32_t)BM && r < rows_valid) ln.sa_ok |= 1u << i;
-      }
-      for (int i = 0; i < SB_IPW; ++i) {
-        const uint32_t byte = (wave * SB_IPW + i) * 256 + lane * 4;
+    ln.sc_ok = 0;
+    for (int i = 0; i < SC_IPW; ++i) {
+      const ScSlot sl = sc_slot(wave, i);
+      ln.sc_off[i] = kOob;
+      if (sl.kind == 0) {
+        const uint32_t r = sl.idx * 64 + lane;
+        ln.sc_off[i] = (uint32_t)((int64_t)r * ldsa);
+        if (r < rows_valid) ln.sc_ok |= 1u << i;
+      } else if (sl.kind == 1) {
+        const uint32_t byte = sl.idx * 256 + lane * 4;
         const uint32_t e = byte / BN, col = byte % BN;
-        ln.sb_off[i] = (uint32_t)((int64_t)e * ldsb) + col;
-        if (e < 4 && n_tile * BN + col < N) ln.sb_ok |= 1u << i;
+        ln.sc_off[i] = (uint32_t)((int64_t)e * ldsb) + col;
+        if (n_tile * BN + col < N) ln.sc_ok |= 1u << i;
       }
     }
   }
@@ -320,24 +324,28 @@ struct DmaKernel {
   // Scales: this family runs MX only with K a multiple of the stage depth,
   // so a stage inside [0, kend) has all 4 blocks; a padding stage past kend
   // reads none.
-  __host__ __device__ __forceinline__ static Access sa_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
-    const bool ok = ((ln.sa_ok >> i) & 1u) && kb0 < kend;
-    return Access{ok, ok ? ln.sa_off[i] : kOob};
-  }
-  __host__ __device__ __forceinline__ static Access sb_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
-    const bool ok = ((ln.sb_ok >> i) & 1u) && kb0 < kend;
-    return Access{ok, ok ? ln.sb_off[i] : kOob};
+  __host__ __device__ __forceinline__ static Access sc_access(const Lanes& ln, int i, uint32_t kb0, uint32_t kend) {
+    const bool ok = ((ln.sc_ok >> i) & 1u) && kb0 < kend;
+    return Access{ok, ok ? ln.sc_off[i] : kOob};
   }
   // LDS byte offsets, inside a stage, of DMA instruction i of a wave.
   __host__ __device__ __forceinline__ static uint32_t a_lds(uint32_t wave, int i) { return (wave * A_IPW + i) * 1024; }
   __host__ __device__ __forceinline__ static uint32_t b_lds(uint32_t wave, int i) {
     return A_BYTES + (wave * B_IPW + i) * 1024;
   }
-  __host__ __device__ __forceinline__ static uint32_t sa_lds(uint32_t wave, int i) {
-    return A_BYTES + B_BYTES + (wave * SA_IPW + i) * 256;
-  }
-  __host__ __device__ __forceinline__ static uint32_t sb_lds(uint32_t wave, int i) {
-    return A_BYTES + B_BYTES + SA_BYTES + (wave * SB_IPW + i) * 256;
+  // Scale slot i of a wave: kind 0 = A instruction idx (rows 64*idx ..),
+  // 1 = B instruction idx (bytes 256*idx .. of the [4][BN] block), 2 = none;
+  // lds: its byte offset inside the stage (for none, the dummy area).
+  struct ScSlot {
+    int kind;
+    uint32_t idx, lds;
+  };
+  __host__ __device__ __forceinline__ static ScSlot sc_slot(uint32_t wave, int i) {
+    const uint32_t x = wave * SC_IPW + (uint32_t)i;
+    if (x < (uint32_t)SA_N) return ScSlot{0, x, A_BYTES + B_BYTES + x * 256u};
+    if (x < (uint32_t)(SA_N + SB_N))
+      return ScSlot{1, x - SA_N, A_BYTES + B_BYTES + SA_BYTES + (x - SA_N) * 256u};
+    return ScSlot{2, 0u, (uint32_t)(A_BYTES + B_BYTES + SA_BYTES + SB_BYTES)};
   }
 
   // Per-task DMA state: buffer descriptors over the task's panels and, for
@@ -350,7 +358,10 @@ struct DmaKernel {
   // zeros and read nothing), so that each stage is exactly LPS
   // instructions for the vmcnt arithmetic.
   struct Dma {
-    u32x4_t ra, rb, rsa, rsb;
+    u32x4_t ra, rb;
+    u32x4_t rsc[SC_IPW > 0 ? SC_IPW : 1];   // scale slot i: its matrix's descriptor,
+    uint32_t sclds[SC_IPW > 0 ? SC_IPW : 1];  // its byte offset inside a stage,
+    uint32_t scb;                             // bit i: slot i reads B's scales
     uint32_t vo[LPS];
   };
 
@@ -363,12 +374,8 @@ struct DmaKernel {
       const int i = X - A_IPW;
       return ((ln.b_ok >> i) & 1u) ? ln.b_off[i] : kOob;
     }
-    if (X < A_IPW + B_IPW + SA_IPW) {
-      const int i = X - A_IPW - B_IPW;
-      return ((ln.sa_ok >> i) & 1u) ? ln.sa_off[i] : kOob;
-    }
-    const int i = X - A_IPW - B_IPW - SA_IPW;
-    return ((ln.sb_ok >> i) & 1u) ? ln.sb_off[i] : kOob;
+    const int i = X - A_IPW - B_IPW;
+    return ((ln.sc_ok >> i) & 1u) ? ln.sc_off[i] : kOob;
   }
 
   template <bool FULL>
@@ -376,9 +383,16 @@ struct DmaKernel {
     Dma d;
     d.ra = make_desc(c.a_tile);
     d.rb = make_desc(c.b_tile);
+    d.scb = 0;
     if constexpr (T::SCALED) {
-      d.rsa = make_desc(c.sa_tile);
-      d.rsb = make_desc(c.sb_tile);
+      const u32x4_t rsa = make_desc(c.sa_tile), rsb = make_desc(c.sb_tile);
+#pragma unroll
+      for (int i = 0; i < SC_IPW; ++i) {
+        const ScSlot sl = sc_slot(c.wave, i);
+        d.rsc[i] = sl.kind == 1 ? rsb : rsa;
+        d.sclds[i] = sl.lds;
+        if (sl.kind == 1) d.scb |= 1u << i;
+      }
     }
     if constexpr (FULL) {
 #pragma unroll
@@ -407,14 +421,12 @@ struct DmaKernel {
       constexpr int i = X - A_IPW;
       const uint32_t v = FULL ? d.vo[X] : b_access(c.ln, i, so.kb0, c.kend).voff;
       dma16(d.rb, base + b_lds(c.wave, i), v, so.b);
-    } else if constexpr (X < A_IPW + B_IPW + SA_IPW) {
-      constexpr int i = X - A_IPW - B_IPW;
-      const uint32_t v = FULL ? d.vo[X] : sa_access(c.ln, i, so.kb0, c.kend).voff;
-      dma4(d.rsa, base + sa_lds(c.wave, i), v, so.sa);
     } else {
-      constexpr int i = X - A_IPW - B_IPW - SA_IPW;
-      const uint32_t v = FULL ? d.vo[X] : sb_access(c.ln, i, so.kb0, c.kend).voff;
-      dma4(d.rsb, base + sb_lds(c.wave, i), v, so.sb);
+      // a scale slot: the selects are wave-uniform, so they stay scalar and
+      // add no branch to the step
+      constexpr int i = X - A_IPW - B_IPW;
+      const uint32_t v = FULL ? d.vo[X] : sc_access(c.ln, i, so.kb0, c.kend).voff;
+      dma4(d.rsc[i], base + d.sclds[i], v, ((d.scb >> i) & 1u) ? so.sb : so.sa);
     }
   }
 

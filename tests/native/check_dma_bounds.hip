@@ -165,36 +165,49 @@ void check(const Problem& p) {
                       "B chunk (%lld,%lld) at lds %u", (long long)k, (long long)c, lb);
             }
             if (KN::T::SCALED && p.scaled) {
-              for (int i = 0; i < KN::SA_IPW; ++i) {
-                const uint32_t lds = KN::sa_lds(w, i) + lane * 4;
-                REQUIRE(lds + 4 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES), "SA lds");
-                const auto x = KN::sa_access(ln, i, kb0, k1);
+              for (int i = 0; i < KN::SC_IPW; ++i) {
+                const auto sl = KN::sc_slot(w, i);
+                const auto x = KN::sc_access(ln, i, kb0, k1);
                 ++g_checked;
                 if (full)
                   REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + i), x.voff),
-                          "SA full voff");
+                          "scale full voff");
+                if (sl.kind == 2) {  // padding slot: no access, writes the stage's dummy area
+                  REQUIRE(!x.ok && x.voff == kOob, "padding scale slot accesses memory");
+                  REQUIRE(KN::SD_BYTES == 256 &&
+                              sl.lds == (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES + KN::SB_BYTES) &&
+                              sl.lds + 256 == (uint32_t)KN::STAGE_BYTES,
+                          "padding slot lds %u", sl.lds);
+                  continue;
+                }
+                const uint32_t lds = sl.lds + lane * 4;
+                if (sl.kind == 0)
+                  REQUIRE(lds >= (uint32_t)(KN::A_BYTES + KN::B_BYTES) &&
+                              lds + 4 <= (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES),
+                          "SA lds %u", lds);
+                else
+                  REQUIRE(lds >= (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES) &&
+                              lds + 4 <= (uint32_t)KN::STAGE_BYTES, "SB lds %u", lds);
                 if (!x.ok) continue;
-                const int64_t addr = tk.row0 * a.ldsa + kb0 / 32 + x.voff;
-                const int64_t R = addr / a.ldsa, c = addr % a.ldsa;
-                REQUIRE(R >= row_lo && R < row_hi && c + 4 <= a.ldsa && c == kb0 / 32,
-                        "%s SA row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
-                covSA[R - tk.row0]++;
-              }
-              for (int i = 0; i < KN::SB_IPW; ++i) {
-                const uint32_t lds = KN::sb_lds(w, i) + lane * 4;
-                REQUIRE(lds + 4 <= (uint32_t)KN::STAGE_BYTES, "SB lds");
-                const auto x = KN::sb_access(ln, i, kb0, k1);
-                ++g_checked;
-                if (full)
-                  REQUIRE(same(KN::full_voff(ln, KN::A_IPW + KN::B_IPW + KN::SA_IPW + i),
-                               x.voff),
-                          "SB full voff");
-                if (!x.ok) continue;
-                const int64_t addr = (int64_t)tk.n * BN + (int64_t)(kb0 / 32) * a.ldsb + x.voff;
-                const int64_t R = addr / a.ldsb, c = addr % a.ldsb;
-                REQUIRE(R >= kb0 / 32 && R < kb0 / 32 + 4 && R < p.K / 32 && c + 4 <= p.N,
-                        "%s SB row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
-                for (int e = 0; e < 4; ++e) covSB[(R - kb0 / 32) * BN + (c - tk.n * BN) + e]++;
+                if (sl.kind == 0) {
+                  const int64_t addr = tk.row0 * a.ldsa + kb0 / 32 + x.voff;
+                  const int64_t R = addr / a.ldsa, c = addr % a.ldsa;
+                  REQUIRE(R >= row_lo && R < row_hi && c + 4 <= a.ldsa && c == kb0 / 32,
+                          "%s SA row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
+                  // the row's dword lands where the MFMA operand read expects it
+                  REQUIRE(lds == (uint32_t)(KN::A_BYTES + KN::B_BYTES + (R - tk.row0) * 4),
+                          "SA row %lld at lds %u", (long long)R, lds);
+                  covSA[R - tk.row0]++;
+                } else {
+                  const int64_t addr = (int64_t)tk.n * BN + (int64_t)(kb0 / 32) * a.ldsb + x.voff;
+                  const int64_t R = addr / a.ldsb, c = addr % a.ldsb;
+                  REQUIRE(R >= kb0 / 32 && R < kb0 / 32 + 4 && R < p.K / 32 && c + 4 <= p.N,
+                          "%s SB row %lld col %lld", p.name.c_str(), (long long)R, (long long)c);
+                  const int64_t e = R - kb0 / 32, cc = c - tk.n * BN;
+                  REQUIRE(lds == (uint32_t)(KN::A_BYTES + KN::B_BYTES + KN::SA_BYTES + e * BN + cc),
+                          "SB (%lld,%lld) at lds %u", (long long)e, (long long)cc, lds);
+                  for (int q = 0; q < 4; ++q) covSB[e * BN + cc + q]++;
+                }
               }
             }
           }
