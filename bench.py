@@ -124,11 +124,13 @@ def parse():
     return p.parse_args()
 
 
-def time_launches(fn, steps, warmup):
+def time_launches(fn, steps, warmup, min_warm_s=0.1):
     """Run fn() `warmup` times eagerly, capture `steps` calls of fn() in one
     HIP graph (so host launch overhead does not enter the timing), replay it
-    once untimed, then time one replay between two events on the launch
-    stream.  Returns (total ms, ms per launch)."""
+    untimed until at least min_warm_s of GPU work has run (an idle GPU's
+    clock takes that long to ramp up; the first workload of a process was
+    otherwise measured up to 15% slow), then time one replay between two
+    events on the launch stream.  Returns (total ms, ms per launch)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -137,8 +139,12 @@ def time_launches(fn, steps, warmup):
     with torch.cuda.graph(g):
         for _ in range(steps):
             fn()
-    g.replay()
-    torch.cuda.synchronize()
+    t_end = time.perf_counter() + min_warm_s
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     st = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
