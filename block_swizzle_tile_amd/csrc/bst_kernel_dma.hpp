@@ -353,10 +353,8 @@ struct DmaKernel {
   // padding stage), each instruction's lane offset with the lane's row /
   // column validity folded in (kOob outside).  The K position of a stage
   // reaches the address through the instruction's scalar offset, so a
-  // steady-state DMA is an M0 write and the load.  Without block scales the
-  // scale slots still issue, with every lane out of range (they write
-  // zeros and read nothing), so that each stage is exactly LPS
-  // instructions for the vmcnt arithmetic.
+  // steady-state DMA is an M0 write and the load.  Kernels without block
+  // scales have no scale slots.
   struct Dma {
     u32x4_t ra, rb;
     u32x4_t rsc[SC_IPW > 0 ? SC_IPW : 1];   // scale slot i: its matrix's descriptor,
@@ -542,7 +540,7 @@ struct DmaKernel {
   // The DMA instructions that MFMA slot Q of a stage carries.  A wave
   // blocks while it issues a DMA instruction and its MFMA pipe drains
   // meanwhile, so each one sits right behind an MFMA instead of in a burst.
-  // With 3 or 4 stages the LPS instructions are dealt out evenly over the
+  // With 3 or more stages the LPS instructions are dealt out evenly over the
   // NMF slots; with 2 the stage in flight has only the current stage's
   // compute to land in, so its instructions go one per slot from the first.
   static constexpr int DSLOTS = (STAGES == 2 && LPS < NMF) ? LPS : NMF;
@@ -565,7 +563,7 @@ struct DmaKernel {
   // compile time, so the accumulators never pass through a branch and the
   // steady state carries no per-instruction conditions.
   //
-  // Ring (3 or 4 stages): the MFMAs of K step g carry the LDS reads of K
+  // Ring (3 to 6 stages): the MFMAs of K step g carry the LDS reads of K
   // step g+PD, which may lie in the next stage (resident from the top of
   // the step on), and the step's share of the DMA of stage kt+STAGES-1.
   // PD+1 K steps of operands live in registers, in a ring of sets.
