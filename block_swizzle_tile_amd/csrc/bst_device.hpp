@@ -210,6 +210,21 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t G) {
   return remap ? lw : w;
 }
 
+// The value x, as if computed at this point: whatever the compiler derives
+// from the result stays after it.  Lane and wave indices pass through this
+// at the start of each task's set-up and epilogue; otherwise the compiler
+// hoists every per-lane address and mask (all loop-invariant across the
+// tasks of a persistent workgroup) to the kernel's start, where they stay
+// live across the K loop and the large tiles spill them to scratch.
+__device__ __forceinline__ uint32_t fresh_v(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t fresh_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 __device__ __forceinline__ uint32_t xcc_id() {
   // HW_REG_XCC_ID (hardware register 20), bits [3:0]
   return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xf;
@@ -331,8 +346,8 @@ struct Epilogue {
                                                               uint32_t t) {
     if (a.split <= 1) return true;
     __shared__ uint32_t last_flag;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = fresh_s(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    const uint32_t lane = fresh_v(threadIdx.x & 63u);
     const size_t tile_bytes = (size_t)BM * BN * 4;
     const uint32_t wave_off = wave * FM * FN * 4096u + lane * 16u;
     {
@@ -463,7 +478,9 @@ struct Epilogue {
     constexpr int NTH = 64 * WM * WN;
     constexpr int CPR = BN * OS / 16;  // 16-byte chunks per row
     constexpr bool STAGED = FULL && SB > 0 && BM * PITCH <= SB && (BM * CPR) % NTH == 0;
-    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t lane = fresh_v(threadIdx.x & 63u);
+    wm = fresh_s(__builtin_amdgcn_readfirstlane(wm));  // wave-uniform in both families
+    wn = fresh_s(__builtin_amdgcn_readfirstlane(wn));
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
     uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
                             (int64_t)tk.n * BN) * OS;
@@ -570,7 +587,7 @@ struct Epilogue {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < BM * CPR / NTH; ++i) {
-        const uint32_t q = threadIdx.x + (uint32_t)i * NTH;
+        const uint32_t q = fresh_v(threadIdx.x) + (uint32_t)i * NTH;
         const uint32_t row = q / CPR, c = q % CPR;
         const u32x4_t v = *(const lds_u32x4_out_t*)(stage + row * PITCH + c * 16);
         *(u32x4_t*)__builtin_assume_aligned(cbase + (int64_t)row * a.ldc * OS + c * 16, 16) = v;

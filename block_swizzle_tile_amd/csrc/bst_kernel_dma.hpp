@@ -575,10 +575,14 @@ struct DmaKernel {
   static constexpr int RING_K = UNR * KSTEPS;  // K steps per loop trip
   // The ring's read-ahead: as far as 3 K steps (and never past the next
   // stage), with a set count that divides the K steps of one trip so that
-  // every set index is a compile-time constant.
+  // every set index is a compile-time constant, and with the accumulators
+  // and operand sets together in at most half of a wave's share of the
+  // SIMD's 512 registers (the rest holds addresses and DMA offsets; wide
+  // MX tiles at read-ahead 2 spilled inside the K loop).
+  static constexpr int SET_REGS = (FM + FN) * T::FRAG_DW + (T::SCALED ? FM + FN : 0);
   static constexpr int ring_pd() {
     for (int dd = (KSTEPS < 3 ? KSTEPS : 3); dd > 1; --dd)
-      if (RING_K % (dd + 1) == 0) return dd;
+      if (RING_K % (dd + 1) == 0 && FM * FN * 16 + (dd + 1) * SET_REGS <= 256 * 4 / NW) return dd;
     return 1;
   }
   static constexpr int PD = ring_pd();
@@ -807,8 +811,8 @@ struct DmaKernel {
       c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
       c.k0 = k0;
       c.kend = k1;
-      lane_setup(c.ln, c.wave, threadIdx.x & 63u, tk.rows_valid, tk.n, a.N, a.lda, c.ldb_bytes,
-                 a.ldsa, a.ldsb);
+      lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
+                 c.ldb_bytes, a.ldsa, a.ldsb);
       if (nk > 0 && full_task(k0, k1))
         task<true>(a, c, tk, s, t, nk, wm, wn, t_start);
       else
