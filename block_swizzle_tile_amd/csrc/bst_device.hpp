@@ -444,6 +444,15 @@ struct Epilogue {
     return true;
   }
 
+  // Rows per staging pass of a whole tile through SB bytes of LDS (rows of
+  // PITCH bytes): the most rows, a multiple of 32 dividing BM, that fit and
+  // that the NTH threads copy out in whole 16-byte chunks; 0 if none.
+  static constexpr int stage_rows(int bm, int pitch, int sb, int cpr, int nth) {
+    for (int rp = bm; rp >= 32; rp -= 32)
+      if (bm % rp == 0 && rp * pitch <= sb && (rp * cpr) % nth == 0) return rp;
+    return 0;
+  }
+
   // Two output elements packed into one dword, rounded to nearest even
   // (the gfx950 conversions round that way in the default mode).
   template <int OUT>
@@ -463,12 +472,13 @@ struct Epilogue {
   // writes its 4 consecutive values with one vector store and no mask.
   //
   // SB > 0: `stage` is SB bytes of LDS the workgroup no longer needs.  A
-  // whole tile that fits (rows padded by 16 bytes) goes through it: the
-  // waves write their values row-major into LDS, then every thread stores
-  // consecutive 16-byte chunks, so a store instruction writes whole cache
-  // lines instead of 16 bytes in each of 32 rows (those partial lines stay
-  // dirty in L2 and cost their write-back when the kernel ends).  All waves
-  // of the workgroup call this together (it has barriers).
+  // whole tile goes through it, in passes of as many rows as fit (rows
+  // padded by 16 bytes): the waves write the pass's values row-major into
+  // LDS, then every thread stores consecutive 16-byte chunks, so a store
+  // instruction writes whole cache lines instead of 16 bytes in each of 32
+  // rows (those partial lines stay dirty in L2 and cost their write-back
+  // when the kernel ends).  All waves of the workgroup call this together
+  // (it has barriers).
   template <int OUT, bool DEQ, bool FULL, int SB>
   __device__ static __forceinline__ void store_as(const GemmArgs& a, const Task& tk,
                                                   const Acc (&acc)[FM][FN], uint32_t wm,
@@ -477,7 +487,14 @@ struct Epilogue {
     constexpr int PITCH = BN * OS + 16;
     constexpr int NTH = 64 * WM * WN;
     constexpr int CPR = BN * OS / 16;  // 16-byte chunks per row
-    constexpr bool STAGED = FULL && SB > 0 && BM * PITCH <= SB && (BM * CPR) % NTH == 0;
+    // Tile rows per staging pass.  Several passes only for 16-bit outputs
+    // and without in-place dequant scale loads (PRE below): the other
+    // combinations spilled over the pass loop.
+    constexpr int RP0 = stage_rows(BM, PITCH, SB, CPR, NTH);
+    constexpr bool MULTI = OS == 2 && !(DEQ && FN * 16 + FM > 40);
+    constexpr int RP = (RP0 == BM || MULTI) ? RP0 : 0;
+    constexpr bool STAGED = FULL && RP > 0;
+    constexpr int NPASS = STAGED ? BM / RP : 1;
     const uint32_t lane = fresh_v(threadIdx.x & 63u);
     wm = fresh_s(__builtin_amdgcn_readfirstlane(wm));  // wave-uniform in both families
     wn = fresh_s(__builtin_amdgcn_readfirstlane(wn));
@@ -510,8 +527,12 @@ struct Epilogue {
             csv[j][g][r] = (FULL || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
         }
     }
+    // One pass: the wave's rows (those of staging pass `pass` when staged).
+    auto emit = [&](uint32_t pass) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if constexpr (STAGED)
+        if ((wm * TM + i * 32) / RP != pass) continue;  // wave-uniform
       const uint32_t ml = wm * TM + i * 32 + l32;
       if (!FULL && ml >= tk.rows_valid) continue;
       uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
@@ -552,7 +573,7 @@ struct Epilogue {
           }
           uint8_t* p = crow + nl * OS;
           if constexpr (STAGED) {
-            lds_byte_t* q = stage + ml * PITCH + nl * OS;
+            lds_byte_t* q = stage + (ml - pass * RP) * PITCH + nl * OS;
             if constexpr (OS == 2)
               *(__attribute__((address_space(3))) u32x2_t*)q =
                   u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
@@ -583,17 +604,27 @@ struct Epilogue {
           }
         }
     }
+    };
     if constexpr (STAGED) {
-      __syncthreads();
+      // a loop, not unrolled: each wave writes in the passes that hold its
+      // rows, and one copy of the code serves them all
+#pragma unroll 1
+      for (uint32_t pass = 0; pass < (uint32_t)NPASS; ++pass) {
+        emit(pass);
+        __syncthreads();
 #pragma unroll
-      for (int i = 0; i < BM * CPR / NTH; ++i) {
-        const uint32_t q = fresh_v(threadIdx.x) + (uint32_t)i * NTH;
-        const uint32_t row = q / CPR, c = q % CPR;
-        const u32x4_t v = *(const lds_u32x4_out_t*)(stage + row * PITCH + c * 16);
-        *(u32x4_t*)__builtin_assume_aligned(cbase + (int64_t)row * a.ldc * OS + c * 16, 16) = v;
+        for (int i = 0; i < RP * CPR / NTH; ++i) {
+          const uint32_t q = fresh_v(threadIdx.x) + (uint32_t)i * NTH;
+          const uint32_t row = q / CPR, c = q % CPR;
+          const u32x4_t v = *(const lds_u32x4_out_t*)(stage + row * PITCH + c * 16);
+          *(u32x4_t*)__builtin_assume_aligned(
+              cbase + (int64_t)(pass * RP + row) * a.ldc * OS + c * 16, 16) = v;
+        }
+        // the next pass (or the next task's prologue) refills the buffer
+        __syncthreads();
       }
-      // the next task's prologue refills the stage buffers
-      __syncthreads();
+    } else {
+      emit(0);
     }
   }
 
