@@ -118,6 +118,12 @@ def parse():
                    help="time every workload configuration (one JSON line per schedule)")
     p.add_argument("--traffic-from", default="",
                    help="write profiles/traffic_fp16_2k.json from the PMC runs under this folder")
+    p.add_argument("--large", action="store_true",
+                   help="time fp16 and MX-fp8 GEMMs at 4096^3 and 8192x8192x4096 (256x256 tiles) "
+                        "and the library GEMMs torch calls for the same shapes")
+    p.add_argument("--clock", action="store_true",
+                   help="with the cycle-accounting build (python -m block_swizzle_tile_amd.build "
+                        "--trace): the shader clock each workload's workgroups ran at")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run plain 256 MiB device copies (the known-size reference that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -249,6 +255,142 @@ def all_configs(args, bst, I, gpu, torch):
     return out
 
 
+LARGE_SHAPES = [("f16", 4096, 4096, 4096), ("f16", 8192, 8192, 4096),
+                ("mx", 4096, 4096, 4096), ("mx", 8192, 8192, 4096)]
+
+
+def large_operands(torch, wl, M, N, K, seed):
+    """Seeded synthetic operands of a large shape, made on the device: fp16
+    uniform[-1, 1]; MX-fp8 e4m3 from N(0, 1) with e8m0 block scales drawn
+    from 2^-4 .. 2^4 (the recipes of the 1024-size workloads, scaled up)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    if wl == "f16":
+        A = (torch.rand((M, K), device="cuda", generator=g) * 2 - 1).half()
+        B = (torch.rand((K, N), device="cuda", generator=g) * 2 - 1).half()
+        return A, B, torch.empty((M, N), dtype=torch.float16, device="cuda"), {}
+    A = torch.randn((M, K), device="cuda", generator=g).to(torch.float8_e4m3fn)
+    B = torch.randn((K, N), device="cuda", generator=g).to(torch.float8_e4m3fn)
+    sa = torch.randint(123, 132, (M, K // 32), device="cuda", generator=g, dtype=torch.int32)
+    sb = torch.randint(123, 132, (K // 32, N), device="cuda", generator=g, dtype=torch.int32)
+    kw = dict(scale_a=sa.to(torch.uint8), scale_b=sb.to(torch.uint8))
+    return A, B, torch.empty((M, N), dtype=torch.bfloat16, device="cuda"), kw
+
+
+def event_time(torch, fn, n):
+    """ms per call of fn() over n eager calls between two events (after 5
+    untimed calls and at least 0.1 s of warm-up work)."""
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        fn()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def large(args, bst, torch):
+    """Large shapes at the 256x256 tile (Zn, offset 4, XCD remap), beside the
+    library GEMMs torch calls on the same device (hipBLASLt: fp16 with B
+    row-major as here, and with B stored transposed; MX-fp8 through
+    torch._scaled_mm with e8m0 block scales, B stored transposed)."""
+    for i, (wl, M, N, K) in enumerate(LARGE_SHAPES):
+        A, B, C, kw = large_operands(torch, wl, M, N, K, 1000 + i)
+        flop = 2.0 * M * N * K
+        peak = PEAK["f16" if wl == "f16" else "e4m3"]
+        s = bst.make_sched(tile=(256, 256), offset=4, direction="zn", xcd_remap=1)
+        runs = [("bst 256x256", lambda: bst.gemm(A, B, C, sched=s, **kw))]
+        if wl == "f16":
+            Bt = B.t().contiguous().t()
+            runs += [("torch.matmul (B row-major)", lambda: torch.matmul(A, B)),
+                     ("torch.matmul (B transposed)", lambda: torch.matmul(A, Bt))]
+        else:
+            Bt = B.t().contiguous().t()
+            e8 = torch.float8_e8m0fnu
+            sa = kw["scale_a"].view(e8)
+            sbt = kw["scale_b"].t().contiguous().view(e8)
+            runs += [("torch._scaled_mm (B transposed)",
+                      lambda: torch._scaled_mm(A, Bt, scale_a=sa, scale_b=sbt,
+                                               out_dtype=torch.bfloat16))]
+        for name, fn in runs:
+            try:
+                ms = event_time(torch, fn, 20)
+            except Exception as ex:  # a library path this torch build lacks
+                print(json.dumps({"shape": [M, N, K], "dtype": wl, "impl": name,
+                                  "error": repr(ex)[:200]}), flush=True)
+                continue
+            tf = flop / (ms * 1e-3) / 1e12
+            print(json.dumps({"shape": [M, N, K], "dtype": wl, "impl": name,
+                              "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                              "pct_of_peak": round(100.0 * tf / peak, 1)}), flush=True)
+        del A, B, C, kw
+
+
+def clock(args, torch, np, I, gpu):
+    """Shader clock during each workload, from the cycle-accounting build:
+    every workgroup records the 100 MHz reference counter at its start and
+    end and the shader cycles in between (30 untimed launches first, so the
+    clock has settled)."""
+    import ctypes
+    from block_swizzle_tile_amd import _lib as L
+    from block_swizzle_tile_amd import build as bld
+    if not os.path.exists(bld.TRACE_LIB):
+        sys.exit("bench.py --clock needs %s (python -m block_swizzle_tile_amd.build --trace)"
+                 % bld.TRACE_LIB)
+    L.LIB_PATH = bld.TRACE_LIB
+    import block_swizzle_tile_amd as bst
+    lib = L.lib()
+    lib.bst_debug_set_trace.argtypes = [ctypes.c_void_p]
+    lib.bst_debug_set_trace.restype = None
+    tr = torch.zeros(128 + 4 * 256, dtype=torch.int64, device="cuda")
+
+    def one(name, fn):
+        lib.bst_debug_set_trace(None)
+        for _ in range(30):
+            fn()
+        torch.cuda.synchronize()
+        tr.zero_()
+        lib.bst_debug_set_trace(ctypes.c_void_p(tr.data_ptr()))
+        fn()
+        torch.cuda.synchronize()
+        lib.bst_debug_set_trace(None)
+        t = tr.cpu()[128:].view(256, 4)
+        t = t[t[:, 3] == 1].double()
+        mhz = t[:, 2] / ((t[:, 1] - t[:, 0]) / 100.0)
+        life = (t[:, 1] - t[:, 0]) / 100.0
+        print(json.dumps({"workload": name, "workgroups": int(t.shape[0]),
+                          "shader_mhz_median": round(float(mhz.median()), 0),
+                          "shader_mhz_min": round(float(mhz.min()), 0),
+                          "shader_mhz_max": round(float(mhz.max()), 0),
+                          "workgroup_life_us_median": round(float(life.median()), 2)}),
+              flush=True)
+
+    w = I.workload("fp16_2k")
+    A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    s = bst.make_sched(tile=(64, 64), offset=8, direction="zn", xcd_remap=1)
+    one("fp16 1024x1024x2048 64x64", lambda: bst.gemm(A, B, C, sched=s))
+    x = I.workload("mxfp8_4k")
+    Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
+    sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
+    Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
+    s = bst.make_sched(tile=(64, 128), offset=8, direction="zn", xcd_remap=1)
+    one("MX-fp8 1024x2048x4096 64x128", lambda: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s))
+    for i, (wl, M, N, K) in enumerate(LARGE_SHAPES):
+        A, B, C, kw = large_operands(torch, wl, M, N, K, 1000 + i)
+        s = bst.make_sched(tile=(256, 256), offset=4, direction="zn", xcd_remap=1)
+        one("%s %dx%dx%d 256x256" % ("fp16" if wl == "f16" else "MX-fp8", M, N, K),
+            lambda: bst.gemm(A, B, C, sched=s, **kw))
+        del A, B, C, kw
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -272,7 +414,6 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}), flush=True)
         return
 
-    import block_swizzle_tile_amd as bst
     from block_swizzle_tile_amd import inputs as I
 
     def gpu(arr, kind):
@@ -285,6 +426,13 @@ def main():
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
 
+    if args.clock:
+        clock(args, torch, np, I, gpu)
+        return
+    import block_swizzle_tile_amd as bst
+    if args.large:
+        large(args, bst, torch)
+        return
     if args.all_configs:
         all_configs(args, bst, I, gpu, torch)
         return

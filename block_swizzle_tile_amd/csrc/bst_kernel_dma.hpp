@@ -761,6 +761,10 @@ struct DmaKernel {
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
     uint64_t t_start = trace_stamp();
+#ifdef BST_TRACE
+    const uint64_t clk_ref0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t clk_sh0 = t_start;
+#endif
     GroupTable* gt = nullptr;
     uint32_t T_tiles = a.tiles;
     if constexpr (GROUPED) {
@@ -820,6 +824,22 @@ struct DmaKernel {
       t_start = trace_stamp();
       u += a.grid;
     } while (u < units);
+#ifdef BST_TRACE
+    // Clock record of the first 256 workgroups at trace[128 + 4 w]: the
+    // 100 MHz reference counter at the start and at the end, and the shader
+    // cycles in between, so shader cycles / reference ticks gives the shader
+    // clock the workgroup ran at.
+    if (a.trace != nullptr && threadIdx.x == 0 && blockIdx.x < 256) {
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint64_t sh1 = __builtin_amdgcn_s_memtime();
+      const uint64_t ref1 = __builtin_amdgcn_s_memrealtime();
+      uint64_t* o = a.trace + 128 + 4 * blockIdx.x;
+      o[0] = clk_ref0;
+      o[1] = ref1;
+      o[2] = sh1 - clk_sh0;
+      o[3] = 1;
+    }
+#endif
   }
 };
 
