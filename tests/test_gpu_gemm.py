@@ -121,9 +121,12 @@ def test_k_zero_and_empty(orc):
      dict(tile=(128, 128), offset=2, split_k=4, path=1),
      dict(tile=(256, 128), offset=4, direction="nz", path=1),
      dict(tile=(128, 256), offset=2, split_k=2, path=2),
-     dict(tile=(64, 64), offset=8, path=2, xcd_remap=1)])
+     dict(tile=(64, 64), offset=8, path=2, xcd_remap=1),
+     dict(tile=(256, 256), offset=2, xcd_remap=1),
+     dict(tile=(128, 192), offset=1, path=2)])
 def test_fp16_2k_workload(orc, fp16_2k, sched):
-    """1024x1024x2048 fp16, every swizzle setting at 256x128 plus split-K forms."""
+    """1024x1024x2048 fp16, every swizzle setting at 256x128 plus split-K forms and
+    the tiles whose epilogue stages a whole tile in several passes."""
     w, ref, den = fp16_2k
     say("fp16 2k", sched)
     C = bst().gemm(to_gpu(w["A"], "f16"), to_gpu(w["B"], "f16"),
