@@ -530,80 +530,80 @@ struct Epilogue {
     // One pass: the wave's rows (those of staging pass `pass` when staged).
     auto emit = [&](uint32_t pass) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (STAGED)
-        if ((wm * TM + i * 32) / RP != pass) continue;  // wave-uniform
-      const uint32_t ml = wm * TM + i * 32 + l32;
-      if (!FULL && ml >= tk.rows_valid) continue;
-      uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
-      float rs = 1.0f;
-      if constexpr (PRE)
-        rs = rsv[i];
-      else if constexpr (DEQ)
-        rs = a.row_scale[tk.row0 + ml];
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (STAGED)
+          if ((wm * TM + i * 32) / RP != pass) continue;  // wave-uniform
+        const uint32_t ml = wm * TM + i * 32 + l32;
+        if (!FULL && ml >= tk.rows_valid) continue;
+        uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
+        float rs = 1.0f;
+        if constexpr (PRE)
+          rs = rsv[i];
+        else if constexpr (DEQ)
+          rs = a.row_scale[tk.row0 + ml];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;  // column inside the tile
-          if (!FULL && nl >= tk.nAct) continue;
-          const bool whole = FULL || nl + 4 <= tk.nAct;
-          float f[4];
-          int32_t iv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const auto x = acc[i][j][4 * g + r];
-            if constexpr (T::IS_INT) {
-              iv[r] = x;
-              f[r] = (float)iv[r];
-            } else {
-              f[r] = x;
-              iv[r] = 0;
-            }
-          }
-          if constexpr (PRE) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) f[r] = (f[r] * rs) * csv[j][g][r];
-          } else if constexpr (DEQ) {
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t nl = wn * TN + j * 32 + 8 * g + 4 * hi;  // column inside the tile
+            if (!FULL && nl >= tk.nAct) continue;
+            const bool whole = FULL || nl + 4 <= tk.nAct;
+            float f[4];
+            int32_t iv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float c = (whole || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
-              f[r] = (f[r] * rs) * c;
+              const auto x = acc[i][j][4 * g + r];
+              if constexpr (T::IS_INT) {
+                iv[r] = x;
+                f[r] = (float)iv[r];
+              } else {
+                f[r] = x;
+                iv[r] = 0;
+              }
             }
-          }
-          uint8_t* p = crow + nl * OS;
-          if constexpr (STAGED) {
-            lds_byte_t* q = stage + (ml - pass * RP) * PITCH + nl * OS;
-            if constexpr (OS == 2)
-              *(__attribute__((address_space(3))) u32x2_t*)q =
-                  u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
-            else if constexpr (OUT == OUT_F32)
-              *(__attribute__((address_space(3))) f32x4_t*)q = f32x4_t{f[0], f[1], f[2], f[3]};
-            else
-              *(__attribute__((address_space(3))) i32x4_t*)q = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
-            (void)p;
-          } else if (whole) {
-            if constexpr (OS == 2)
-              *(u32x2_t*)__builtin_assume_aligned(p, 8) =
-                  u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
-            else if constexpr (OUT == OUT_F32)
-              *(f32x4_t*)__builtin_assume_aligned(p, 16) = f32x4_t{f[0], f[1], f[2], f[3]};
-            else
-              *(i32x4_t*)__builtin_assume_aligned(p, 16) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
-          } else {
+            if constexpr (PRE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (nl + r >= tk.nAct) continue;
+              for (int r = 0; r < 4; ++r) f[r] = (f[r] * rs) * csv[j][g][r];
+            } else if constexpr (DEQ) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float c = (whole || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
+                f[r] = (f[r] * rs) * c;
+              }
+            }
+            uint8_t* p = crow + nl * OS;
+            if constexpr (STAGED) {
+              lds_byte_t* q = stage + (ml - pass * RP) * PITCH + nl * OS;
               if constexpr (OS == 2)
-                ((uint16_t*)p)[r] = (uint16_t)pack2<OUT>(f[r], 0.0f);
+                *(__attribute__((address_space(3))) u32x2_t*)q =
+                    u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
               else if constexpr (OUT == OUT_F32)
-                ((float*)p)[r] = f[r];
+                *(__attribute__((address_space(3))) f32x4_t*)q = f32x4_t{f[0], f[1], f[2], f[3]};
               else
-                ((int32_t*)p)[r] = iv[r];
+                *(__attribute__((address_space(3))) i32x4_t*)q = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+              (void)p;
+            } else if (whole) {
+              if constexpr (OS == 2)
+                *(u32x2_t*)__builtin_assume_aligned(p, 8) =
+                    u32x2_t{pack2<OUT>(f[0], f[1]), pack2<OUT>(f[2], f[3])};
+              else if constexpr (OUT == OUT_F32)
+                *(f32x4_t*)__builtin_assume_aligned(p, 16) = f32x4_t{f[0], f[1], f[2], f[3]};
+              else
+                *(i32x4_t*)__builtin_assume_aligned(p, 16) = i32x4_t{iv[0], iv[1], iv[2], iv[3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                if (nl + r >= tk.nAct) continue;
+                if constexpr (OS == 2)
+                  ((uint16_t*)p)[r] = (uint16_t)pack2<OUT>(f[r], 0.0f);
+                else if constexpr (OUT == OUT_F32)
+                  ((float*)p)[r] = f[r];
+                else
+                  ((int32_t*)p)[r] = iv[r];
+              }
             }
           }
-        }
-    }
+      }
     };
     if constexpr (STAGED) {
       // a loop, not unrolled: each wave writes in the passes that hold its
