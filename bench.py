@@ -14,6 +14,12 @@ launches (one HIP-graph replay of them between two events on the launch
 stream) against the fp16 dense MFMA peak
 of MI355X (2.5 PFLOP/s; 5.0 for fp8); `cpu_baseline` times the CPU oracle
 (fp64, OpenMP) on the same workload on this host.
+
+Other modes (one JSON line per measurement): --all-configs (every workload
+configuration), --l2-sweep (every swizzle setting, for rocprofv3 counters),
+--large (4096^3 and 8192x8192x4096 beside the library GEMMs torch calls),
+--clock (shader clock under each workload, with the cycle-accounting build),
+--calib-copy and --traffic-from (HBM traffic calibration and summary).
 """
 import argparse
 import hashlib
