@@ -73,7 +73,8 @@ def _padded(g, rows, cols, ld, kind):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (7, 9, 13), (65, 130, 200), (300, 17, 72),
-                                   (129, 257, 1000), (64, 64, 64), (33, 8, 520)])
+                                   (129, 257, 1000), (64, 64, 64), (33, 8, 520),
+                                   (256, 256, 200), (512, 384, 136)])
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_ragged_shapes(orc, M, N, K, kind):
     g = np.random.default_rng(M * 1000 + N * 10 + K)
