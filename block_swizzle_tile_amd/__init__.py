@@ -28,11 +28,13 @@ __all__ = ["Sched", "BstError", "make_sched", "gemm", "batched_gemm", "grouped_g
 
 
 def make_sched(tile=(0, 0), tile_k=0, offset=1, direction="zn", split_k=1, xcd_remap=0, grid=0,
-               path=0):
+               path=0, shuffle_k=0):
     """A :class:`Sched` from Python values (direction: 'zn', 'nz', 'raster' or 0/1/2;
-    path: 0 automatic, 1 register-staged kernels, 2 LDS-DMA kernels)."""
+    path: 0 automatic, 1 register-staged kernels, 2 LDS-DMA kernels; shuffle_k: 1 rotates
+    each task's K-loop start)."""
     d = _DIRS[direction] if isinstance(direction, str) else int(direction)
-    return Sched(tile[0], tile[1], tile_k, offset, d, split_k, xcd_remap, grid, path)
+    return Sched(tile[0], tile[1], tile_k, offset, d, split_k, xcd_remap, grid, path,
+                 int(shuffle_k))
 
 
 def version():

@@ -28,7 +28,7 @@ EXPORTS = ["bst_gemm", "bst_batched_gemm", "bst_grouped_gemm_slice_m", "bst_quan
 class Sched(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in
                 ("tile_m", "tile_n", "tile_k", "swizzle_offset", "swizzle_direction", "split_k",
-                 "xcd_remap", "grid", "path")]
+                 "xcd_remap", "grid", "path", "shuffle_k")]
 
 
 _lock = threading.Lock()

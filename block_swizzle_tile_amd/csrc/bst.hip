@@ -120,7 +120,7 @@ constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
 struct Plan {
   const Instance* inst = nullptr;
   uint32_t bm = 0, bn = 0, bk = 0;
-  uint32_t off = 1, dir = 0, remap = 0;
+  uint32_t off = 1, dir = 0, remap = 0, shuffle = 0;
   uint32_t split = 1, kslice = 0;
   uint64_t tile_cap = 0;  // tiles (upper bound for grouped)
   uint32_t grid = 0;
@@ -182,6 +182,7 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
     d.tile_n = 128;
   }
   if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
+  if (d.shuffle_k > 1) return fail(BST_E_INVAL, "shuffle_k must be 0 or 1");
   const Instance* reg = find_instance(ab, d.tile_m, d.tile_n, kind == 1, false);
   const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, kind == 1, true);
   if (!reg && !dma)
@@ -203,6 +204,7 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   p.off = d.swizzle_offset;
   p.dir = d.swizzle_direction;
   p.remap = d.xcd_remap;
+  p.shuffle = p.inst->dma ? d.shuffle_k : 0u;  // the register-staged family runs stages in order
   const int64_t loopsN = cdiv64(N, p.bn);
   const int64_t tiles = kind == 1 ? (cdiv64(M, p.bm) + count) * loopsN
                                   : count * cdiv64(M, p.bm) * loopsN;
@@ -324,7 +326,7 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   a.M = (uint32_t)M; a.N = (uint32_t)N; a.K = (uint32_t)K;
   a.batch = (uint32_t)batch;
   a.tiles = (uint32_t)p.tile_cap;
-  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
   return launch(p, a, stream);
@@ -419,7 +421,7 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
   a.G = G;
   a.total_m = total_m;
   a.N = (uint32_t)N; a.K = (uint32_t)K;
-  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
   return launch(p, a, stream);
@@ -445,7 +447,7 @@ bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const
   a.M = (uint32_t)M; a.N = (uint32_t)N;
   a.batch = (uint32_t)batch;
   a.tiles = (uint32_t)p.tile_cap;
-  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
   a.map_out = out;
   uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, a.tiles)
                                : (uint32_t)std::min<int64_t>(device_cus(), a.tiles);
@@ -479,7 +481,7 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
   a.group_m = group_m;
   a.G = G;
   a.total_m = total_m;
-  a.off = p.off; a.dir = p.dir; a.remap = p.remap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
   a.map_out = out;
   uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, (uint32_t)p.tile_cap)
                                : (uint32_t)std::min<int64_t>(device_cus(), p.tile_cap);
@@ -518,6 +520,7 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
   out->xcd_remap = p.remap;
   out->grid = p.grid;
   out->path = p.inst->dma ? 2u : 1u;
+  out->shuffle_k = p.shuffle;
   return BST_OK;
 }
 

@@ -69,6 +69,7 @@ struct GemmArgs {
   uint32_t split;                     // K slices per tile (>= 1)
   uint32_t kslice;                    // K elements per slice (multiple of the stage depth)
   uint32_t remap;                     // XCD-contiguous renumbering of workgroups
+  uint32_t shuffle_k;                 // rotate each whole-stage task's K-loop start (ShuffleK)
   uint32_t grid;                      // workgroups launched (gridDim.x, passed here because the
                                       // kernel would read it from the dispatch packet in host
                                       // memory: about a microsecond at every kernel start)

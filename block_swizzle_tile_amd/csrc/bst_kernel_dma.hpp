@@ -258,6 +258,7 @@ struct DmaKernel {
     uint32_t ldb_bytes32, ldsb32;  // the same, known below 2^31 per panel
     uint32_t k0;             // first K index of the task's slice
     uint32_t kend;
+    uint32_t kshift, nks;    // ShuffleK: stage j runs K stage (j + kshift) mod nks (nks = ~0: off)
     uint32_t wave;
     Lanes ln;
   };
@@ -403,6 +404,14 @@ struct DmaKernel {
   struct Soff {
     uint32_t kb0, a, b, sa, sb;
   };
+  // K index of the task's stage j.  With ShuffleK (whole-stage tasks only)
+  // the stages start at kshift and wrap around; otherwise nks = ~0 and the
+  // stages, padding included, run in order.
+  __device__ static __forceinline__ uint32_t stage_k(const Ctx& c, uint32_t j) {
+    const uint32_t r = j + c.kshift;
+    return c.k0 + (r >= c.nks ? r - c.nks : r) * BK;
+  }
+
   __device__ static __forceinline__ Soff stage_soff(const Ctx& c, uint32_t kb0) {
     return Soff{kb0, kb0 * (uint32_t)ES, kb0 * c.ldb_bytes32, kb0 / 32u, (kb0 / 32u) * c.ldsb32};
   }
@@ -615,7 +624,7 @@ struct DmaKernel {
       barrier_lds();
     }
     tr.released();
-    const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
+    const Soff so = stage_soff(c, stage_k(c, kt + STAGES - 1));
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
@@ -643,7 +652,7 @@ struct DmaKernel {
     wait_vm<WAITN>();
     barrier_lds();
     tr.released();
-    const Soff so = stage_soff(c, c.k0 + (kt + STAGES - 1) * BK);
+    const Soff so = stage_soff(c, stage_k(c, kt + STAGES - 1));
     KFrag g0, g1;
     load_kstep<S, 0>(g0, wm, wn);
     static_for<NMF>([&](auto q) {
@@ -672,7 +681,7 @@ struct DmaKernel {
       // stages 0..STAGES-2 in flight, then stage 0 resident
       static_for<STAGES - 1>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        issue<I, FULL>(c, d, c.k0 + I * BK);
+        issue<I, FULL>(c, d, stage_k(c, I));
       });
       wait_vm<(STAGES - 2) * LPS>();
       barrier_lds();
@@ -700,7 +709,7 @@ struct DmaKernel {
         step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr);
       });
     } else {
-      issue<0, FULL>(c, d, c.k0);
+      issue<0, FULL>(c, d, stage_k(c, 0));
       tr.prologue_done();
       for (; kt + STAGES < nkp; kt += STAGES) {
         step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
@@ -815,9 +824,12 @@ struct DmaKernel {
       c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
       c.k0 = k0;
       c.kend = k1;
+      const bool whole = nk > 0 && full_task(k0, k1);
+      c.kshift = (a.shuffle_k != 0 && whole) ? t % nk : 0u;
+      c.nks = (a.shuffle_k != 0 && whole) ? nk : 0xFFFFFFFFu;
       lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
                  c.ldb_bytes, a.ldsa, a.ldsb);
-      if (nk > 0 && full_task(k0, k1))
+      if (whole)
         task<true>(a, c, tk, s, t, nk, wm, wn, t_start);
       else
         task<false>(a, c, tk, s, t, nk, wm, wn, t_start);

@@ -79,6 +79,13 @@ typedef struct bst_sched {
   uint32_t path;               /* kernel family: 0 = automatic, 1 = register-staged (any shape),
                                   2 = LDS-DMA pipeline (K and N whole 16-byte chunks, MX K a
                                   multiple of 128; BST_E_UNSUPPORTED otherwise) */
+  uint32_t shuffle_k;          /* 1: ShuffleK (a policy flag of the Preload dispatch policies,
+                                  "Block Dispatch Policies"): the K loop of task t starts at
+                                  stage t mod S of its S stages and wraps around, so that tiles
+                                  running together read different K slices.  Applied by the
+                                  LDS-DMA family to tasks of whole stages; others run in order.
+                                  0 = off.  Results differ from 0 only by fp32 summation order
+                                  (int8: bit-identical). */
 } bst_sched;
 
 /*

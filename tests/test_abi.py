@@ -59,6 +59,7 @@ def gemm(L, ab=_lib.F16, c=_lib.F16, M=64, N=64, K=64, A=FAKE, lda=None, B=FAKE,
 def test_validation_errors(L):
     assert gemm(L, sched=S(offset=0)) == _lib.E_INVAL            # offset 0 undefined
     assert gemm(L, sched=S(direction=3)) == _lib.E_INVAL         # no such direction
+    assert gemm(L, sched=S(shuffle_k=2)) == _lib.E_INVAL         # ShuffleK is a flag
     assert gemm(L, M=-1) == _lib.E_INVAL
     assert gemm(L, A=None) == _lib.E_INVAL
     assert gemm(L, C=None) == _lib.E_INVAL
@@ -118,6 +119,23 @@ def test_effective_sched_split_resolution(L):
                                  ctypes.byref(out)) == _lib.E_UNSUPPORTED
     assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 64, ctypes.byref(S(path=3)),
                                  ctypes.byref(out)) == _lib.E_INVAL
+
+
+def test_effective_sched_shuffle_k(L):
+    """ShuffleK is applied by the LDS-DMA family only; the register-staged one runs stages in
+    order and reports 0."""
+    out = _lib.Sched()
+    assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 2048,
+                                 ctypes.byref(S(tile=(64, 64), shuffle_k=1)),
+                                 ctypes.byref(out)) == _lib.OK
+    assert out.path == 2 and out.shuffle_k == 1
+    assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 2048,
+                                 ctypes.byref(S(tile=(64, 64), shuffle_k=1, path=1)),
+                                 ctypes.byref(out)) == _lib.OK
+    assert out.path == 1 and out.shuffle_k == 0
+    assert L.bst_effective_sched(0, _lib.F16, 1, 1024, 1024, 2048,
+                                 ctypes.byref(S(tile=(64, 64))), ctypes.byref(out)) == _lib.OK
+    assert out.shuffle_k == 0
 
 
 def test_grouped_validation(L):

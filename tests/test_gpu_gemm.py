@@ -124,7 +124,10 @@ def test_k_zero_and_empty(orc):
      dict(tile=(128, 256), offset=2, split_k=2, path=2),
      dict(tile=(64, 64), offset=8, path=2, xcd_remap=1),
      dict(tile=(256, 256), offset=2, xcd_remap=1),
-     dict(tile=(128, 192), offset=1, path=2)])
+     dict(tile=(128, 192), offset=1, path=2),
+     dict(tile=(64, 64), offset=8, xcd_remap=1, shuffle_k=1),
+     dict(tile=(128, 128), offset=2, split_k=2, shuffle_k=1),
+     dict(tile=(256, 256), offset=4, shuffle_k=1)])
 def test_fp16_2k_workload(orc, fp16_2k, sched):
     """1024x1024x2048 fp16, every swizzle setting at 256x128 plus split-K forms and
     the tiles whose epilogue stages a whole tile in several passes."""
@@ -172,7 +175,9 @@ def test_mxfp8_small_full(orc):
                   dict(tile=(64, 64), offset=2, direction="nz", split_k=2),
                   dict(tile=(128, 128), path=1), dict(tile=(256, 128), path=1, split_k=2),
                   dict(tile=(256, 128), path=2, offset=3), dict(tile=(64, 64), path=2),
-                  dict(tile=(128, 64), offset=2), dict(tile=(64, 128), split_k=2, xcd_remap=1)]:
+                  dict(tile=(128, 64), offset=2), dict(tile=(64, 128), split_k=2, xcd_remap=1),
+                  dict(tile=(64, 128), offset=2, xcd_remap=1, shuffle_k=1),
+                  dict(tile=(256, 256), offset=4, shuffle_k=1)]:
         say("mxfp8 small", sched)
         C = bst().gemm(A, B, scale_a=sa, scale_b=sb, sched=bst().make_sched(**sched))
         check_close(orc, C, ref, den, TOL_8, str(sched))
@@ -215,7 +220,8 @@ def test_int8_groups_small_full(orc):
     for sched in [dict(tile=(64, 64)), dict(tile=(128, 128), offset=2, direction="nz"),
                   dict(tile=(256, 256), offset=1, split_k=2), dict(tile=(256, 128), xcd_remap=1),
                   dict(tile=(128, 128), path=1), dict(tile=(256, 256), path=1, offset=2),
-                  dict(tile=(64, 64), path=2, split_k=2), dict(tile=(256, 256), path=2)]:
+                  dict(tile=(64, 64), path=2, split_k=2), dict(tile=(256, 256), path=2),
+                  dict(tile=(256, 256), offset=1, shuffle_k=1)]:
         say("int8 groups small", sched)
         s = bst().make_sched(**sched)
         raw = bst().grouped_gemm_slice_m(A, B, gmt, sched=s)
