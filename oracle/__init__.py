@@ -65,6 +65,8 @@ def lib():
             L.orc_grouped_gemm.argtypes = [i32, p, i64, i64, i64, p, i64, p, i64, i64, p, p,
                                            i64, i64, i64, ctypes.c_int, p, i64, p, p, p]
             L.orc_grouped_gemm.restype = ctypes.c_int
+            L.orc_add_addend.argtypes = [i64, p, p, p]
+            L.orc_add_addend.restype = ctypes.c_int
             L.orc_compare.argtypes = [i64, p, p, p, p]
             L.orc_compare.restype = dbl
             _lib = L
@@ -169,6 +171,17 @@ def grouped_gemm(group_m, A, B, N, K, *, row_scale=None, col_scale=None, tile=(1
     if rc != 0:
         raise ValueError("orc_grouped_gemm failed (%d)" % rc)
     return ref, den, acc
+
+
+def gemm_add(ab, A, B, X, x_kind, **kw):
+    """matmul-add oracle C = A . B + X: (ref, den) of gemm() with the addend's exact values
+    (X: raw codes of kind x_kind, the output's shape, or the selected rows when rows= is
+    given) added to ref and their magnitudes to den (orc_add_addend in oracle.c)."""
+    ref, den = gemm(ab, A, B, **kw)
+    x = np.ascontiguousarray(decode(x_kind, X), dtype=np.float64).reshape(ref.shape)
+    if lib().orc_add_addend(ref.size, _ptr(x), _ptr(ref), _ptr(den)) != 0:
+        raise ValueError("orc_add_addend failed")
+    return ref, den
 
 
 def compare(got, ref, den):

@@ -398,6 +398,25 @@ int orc_grouped_gemm(int32_t G, const int32_t *group_m, int64_t total_m, int64_t
   return rc;
 }
 
+/* -------------------------------------------------------- matmul-add ---- */
+
+/*
+ * matmul-add ("Block Dispatch Policies" lists a matmul-add example under its
+ * ping-pong policy; reading: C = A.B + X with X of C's shape and type).
+ * Given the exact A.B in ref and its error scale sum |a*b| in den (from
+ * orc_gemm), adds the addend's exact values x to ref and |x| to den, so that
+ * the compare criterion |got - ref| / den stays a relative error of the
+ * whole sum.  n elements, all arrays float64.
+ */
+int orc_add_addend(int64_t n, const double *x, double *ref, double *den) {
+  if (n < 0 || (n > 0 && (!x || !ref || !den))) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    ref[i] += x[i];
+    den[i] += fabs(x[i]);
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------- compare ----- */
 
 /*
