@@ -116,10 +116,12 @@ def effective_sched(kind, ab, count, M, N, K, sched=None):
     return out
 
 
-def gemm(A, B, C=None, *, out_dtype=None, scale_a=None, scale_b=None, sched=None, workspace=None):
-    """C = A @ B for row-major A[M][K], B[K][N] (fp16, bf16, e4m3fn (+ MX scales) or int8)."""
+def gemm(A, B, C=None, *, out_dtype=None, scale_a=None, scale_b=None, sched=None, workspace=None,
+         add=None):
+    """C = A @ B for row-major A[M][K], B[K][N] (fp16, bf16, e4m3fn (+ MX scales) or int8);
+    with add=X (C's shape and dtype, may be C itself): C = A @ B + X."""
     torch = _torch()
-    _dev(A, B, C, scale_a, scale_b)
+    _dev(A, B, C, scale_a, scale_b, add)
     scaled = scale_a is not None
     ab = _code(A.dtype, scaled)
     if _code(B.dtype, scaled) != ab:
@@ -134,6 +136,13 @@ def gemm(A, B, C=None, *, out_dtype=None, scale_a=None, scale_b=None, sched=None
     c = _code(C.dtype)
     nb = workspace_bytes(0, ab, 1, M, N, K, sched)
     ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(nb, A.device)
+    if add is not None:
+        if add.dtype != C.dtype or tuple(add.shape) != (M, N):
+            raise TypeError("the addend must have C's dtype and shape")
+        check(lib().bst_gemm_add(ab, c, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(add),
+                                 _ld(add), _ptr(C), _ld(C), _ptr(scale_a), _ptr(scale_b),
+                                 _sched(sched), _ptr(ws), wsb, _stream(A.device)))
+        return C
     check(lib().bst_gemm(ab, c, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C), _ld(C),
                          _ptr(scale_a), _ptr(scale_b), _sched(sched), _ptr(ws), wsb,
                          _stream(A.device)))

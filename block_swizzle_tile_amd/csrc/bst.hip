@@ -34,14 +34,15 @@ bst_status fail(bst_status st, const char* fmt, ...) {
 
 int kernel_ab(bst_dtype ab) { return (int)ab; }
 
-const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped, bool dma) {
+const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped, bool dma,
+                              bool add = false) {
   const InstanceList lists[] = {instances_f16(), instances_bf16(), instances_i8(),
                                 instances_fp8(), instances_mxfp8()};
   for (const InstanceList& l : lists)
     for (int i = 0; i < l.count; ++i) {
       const Instance& in = l.begin[i];
       if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
-          in.grouped == grouped && in.dma == dma)
+          in.grouped == grouped && in.dma == dma && in.add == add)
         return &in;
     }
   return nullptr;
@@ -154,7 +155,8 @@ bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, cons
 }
 
 bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
-                     const bst_sched* s, bool need_device, Plan& p, const Layout* L = nullptr) {
+                     const bst_sched* s, bool need_device, Plan& p, const Layout* L = nullptr,
+                     bool add = false) {
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (count < 0 || M < 0 || N < 0 || K < 0)
     return fail(BST_E_INVAL, "negative size (count %lld M %lld N %lld K %lld)", (long long)count,
@@ -183,11 +185,13 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   }
   if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
   if (d.shuffle_k > 1) return fail(BST_E_INVAL, "shuffle_k must be 0 or 1");
-  const Instance* reg = find_instance(ab, d.tile_m, d.tile_n, kind == 1, false);
-  const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, kind == 1, true);
+  // matmul-add runs only the LDS-DMA instances built with the addend epilogue
+  const Instance* reg = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, kind == 1, false);
+  const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, kind == 1, true, add);
   if (!reg && !dma)
     return fail(BST_E_UNSUPPORTED, "no %s kernel for dtype %d with tile %ux%u",
-                kind == 1 ? "grouped" : "plain", (int)ab, d.tile_m, d.tile_n);
+                add ? "matmul-add" : kind == 1 ? "grouped" : "plain", (int)ab, d.tile_m,
+                d.tile_n);
   const Layout lay = L ? *L : Layout{K, N, nullptr, nullptr};
   const bool fits = dma && dma_fits(ab, N, K, d.tile_m, (uint32_t)dma->bk, lay);
   if (d.path == 2 && !fits)
@@ -278,11 +282,12 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
                  const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
                  int64_t strideB, void* C, int64_t ldc, int64_t strideC, const uint8_t* sa,
                  const uint8_t* sb, const float* rs, const float* cs, const bst_sched* s,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 void* ws, size_t ws_bytes, void* stream, const void* X = nullptr,
+                 int64_t ldx = 0) {
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
   Plan p;
-  bst_status st = make_plan(0, ab, batch, M, N, K, s, false, p);
+  bst_status st = make_plan(0, ab, batch, M, N, K, s, false, p, nullptr, X != nullptr);
   if (st != BST_OK) return st;
   if (batch == 0 || M == 0 || N == 0) return BST_OK;
   const size_t es = elem_size(ab), ec = elem_size(c);
@@ -296,12 +301,18 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
     return fail(BST_E_INVAL, "negative batch stride");
   if (ab == BST_MXE4M3 && has_k && (!sa || !sb)) return fail(BST_E_INVAL, "MX scales are NULL");
   if ((rs == nullptr) != (cs == nullptr)) return fail(BST_E_INVAL, "give both dequant scales or neither");
+  if (X && (batch != 1 || rs)) return fail(BST_E_INVAL, "the addend is taken by bst_gemm_add only");
+  if (X && ldx < N)
+    return fail(BST_E_INVAL, "leading dimension too small (ldx %lld N %lld)", (long long)ldx,
+                (long long)N);
+  if (X && (!aligned16(X) || !stride_ok(ldx, ec)))
+    return fail(BST_E_ALIGN, "the addend and its stride must be 16-byte multiples");
   if (!aligned16(C) || !stride_ok(ldc, ec) || (batch > 1 && !stride_ok(strideC, ec)) ||
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
                  (batch > 1 && (!stride_ok(strideA, es) || !stride_ok(strideB, es))))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
   const Layout lay{lda, ldb, sa, sb};
-  st = make_plan(0, ab, batch, M, N, K, s, true, p, &lay);
+  st = make_plan(0, ab, batch, M, N, K, s, true, p, &lay, X != nullptr);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
@@ -313,6 +324,8 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   a.A = static_cast<const uint8_t*>(A);
   a.B = static_cast<const uint8_t*>(B);
   a.C = static_cast<uint8_t*>(C);
+  a.X = static_cast<const uint8_t*>(X);
+  a.ldx = ldx;
   a.lda = lda; a.ldb = ldb; a.ldc = ldc;
   a.strideA = batch > 1 ? strideA : 0;
   a.strideB = batch > 1 ? strideB : 0;
@@ -352,6 +365,17 @@ bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K, 
     return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
   return dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
                nullptr, s, ws, ws_bytes, stream);
+}
+
+bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K, const void* A,
+                        int64_t lda, const void* B, int64_t ldb, const void* X, int64_t ldx,
+                        void* C, int64_t ldc, const uint8_t* scale_a, const uint8_t* scale_b,
+                        const bst_sched* s, void* ws, size_t ws_bytes, void* stream) {
+  if (ab != BST_MXE4M3 && (scale_a || scale_b))
+    return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
+  if (M > 0 && N > 0 && !X) return fail(BST_E_INVAL, "the addend X is NULL");
+  return dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
+               nullptr, s, ws, ws_bytes, stream, X, ldx);
 }
 
 bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,

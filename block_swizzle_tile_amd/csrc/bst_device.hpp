@@ -52,6 +52,8 @@ struct GemmArgs {
   const uint8_t* A;
   const uint8_t* B;
   uint8_t* C;
+  const uint8_t* X;                   // matmul-add: addend of C's type and shape, or null
+  int64_t ldx;                        // its leading dimension (elements)
   int64_t lda, ldb, ldc;              // elements
   int64_t strideA, strideB, strideC;  // elements; batch (or group, for B) strides
   const uint8_t* sa;                  // MX scales of A [M][ldsa]
@@ -480,7 +482,7 @@ struct Epilogue {
   // rows (those partial lines stay dirty in L2 and cost their write-back
   // when the kernel ends).  All waves of the workgroup call this together
   // (it has barriers).
-  template <int OUT, bool DEQ, bool FULL, int SB>
+  template <int OUT, bool DEQ, bool FULL, int SB, bool ADD>
   __device__ static __forceinline__ void store_as(const GemmArgs& a, const Task& tk,
                                                   const Acc (&acc)[FM][FN], uint32_t wm,
                                                   uint32_t wn, lds_byte_t* stage) {
@@ -502,6 +504,8 @@ struct Epilogue {
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
     uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
                             (int64_t)tk.n * BN) * OS;
+    // matmul-add (plain GEMM only, so the task's row0 is its first row of X)
+    const uint8_t* xbase = ADD ? a.X + (tk.row0 * a.ldx + (int64_t)tk.n * BN) * OS : nullptr;
     // Dequant scales are gathered before the first store when they fit in a
     // few registers: a store counts in vmcnt too, so a scale load issued
     // after one waits for it (the compiler cannot hoist the loads itself,
@@ -537,6 +541,7 @@ struct Epilogue {
         const uint32_t ml = wm * TM + i * 32 + l32;
         if (!FULL && ml >= tk.rows_valid) continue;
         uint8_t* crow = cbase + (int64_t)ml * a.ldc * OS;
+        const uint8_t* xrow = ADD ? xbase + (int64_t)ml * a.ldx * OS : nullptr;
         float rs = 1.0f;
         if constexpr (PRE)
           rs = rsv[i];
@@ -572,6 +577,7 @@ struct Epilogue {
                 f[r] = (f[r] * rs) * c;
               }
             }
+            if constexpr (ADD) add_x<OUT>(f, iv, xrow + nl * OS, whole, tk.nAct - nl);
             uint8_t* p = crow + nl * OS;
             if constexpr (STAGED) {
               lds_byte_t* q = stage + (ml - pass * RP) * PITCH + nl * OS;
@@ -629,30 +635,82 @@ struct Epilogue {
     }
   }
 
-  template <bool DEQ, bool FULL, int SB>
+  template <bool DEQ, bool FULL, int SB, bool ADD = false>
   __device__ static __forceinline__ void store_kind(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
                                                     uint32_t wn, lds_byte_t* stage) {
     if (a.cdtype == OUT_F16)
-      store_as<OUT_F16, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_F16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
     else if (a.cdtype == OUT_BF16)
-      store_as<OUT_BF16, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_BF16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
     else if (a.cdtype == OUT_F32)
-      store_as<OUT_F32, DEQ, FULL, SB>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_F32, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
     else if constexpr (T::IS_INT && !DEQ)
-      store_as<OUT_I32, false, FULL, SB>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_I32, false, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
+  }
+
+  // matmul-add: the addend's four values at p (of the output kind OUT) are
+  // added to the lane's values before they are rounded; `whole`: all four
+  // columns are inside the problem, else only the first `left` are read.
+  template <int OUT>
+  __device__ static __forceinline__ void add_x(float (&f)[4], int32_t (&iv)[4],
+                                               const uint8_t* p, bool whole, uint32_t left) {
+    if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
+      uint16_t h[4] = {0, 0, 0, 0};
+      if (whole) {
+        const u32x2_t v = *(const u32x2_t*)__builtin_assume_aligned(p, 8);
+        h[0] = (uint16_t)v[0];
+        h[1] = (uint16_t)(v[0] >> 16);
+        h[2] = (uint16_t)v[1];
+        h[3] = (uint16_t)(v[1] >> 16);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((uint32_t)r < left) h[r] = ((const uint16_t*)p)[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (OUT == OUT_F16)
+          f[r] += (float)__builtin_bit_cast(_Float16, h[r]);
+        else
+          f[r] += __builtin_bit_cast(float, (uint32_t)h[r] << 16);
+      }
+    } else {
+      uint32_t w[4] = {0, 0, 0, 0};
+      if (whole) {
+        const u32x4_t v = *(const u32x4_t*)__builtin_assume_aligned(p, 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t e = v[r];  // copy the element out before using it
+          w[r] = e;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((uint32_t)r < left) w[r] = ((const uint32_t*)p)[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (OUT == OUT_I32)
+          iv[r] = (int32_t)((uint32_t)iv[r] + w[r]);  // int32 addition, wrapping
+        else
+          f[r] += __builtin_bit_cast(float, w[r]);
+      }
+    }
   }
 
   // The wave's whole output: one dispatch per task on the output kind, the
   // dequant and whether the tile is whole, then straight-line stores.
   // Dequantised outputs exist for int8 operands only.  SB, stage: LDS that
   // whole tiles may be staged through (see store_as; SB = 0: none).
-  template <int SB = 0>
+  // ADD: the matmul-add instances, whose epilogue adds a.X (never with the
+  // dequant, which the host rules out for them).
+  template <int SB = 0, bool ADD = false>
   __device__ static __forceinline__ void store_tile(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
                                                     uint32_t wn, lds_byte_t* stage = nullptr) {
     const bool full = tk.rows_valid >= (uint32_t)BM && tk.nAct >= (uint32_t)BN;
-    if constexpr (T::IS_INT) {
+    if constexpr (T::IS_INT && !ADD) {
       if (a.row_scale != nullptr) {
         if (full)
           store_kind<true, true, SB>(a, tk, acc, wm, wn, stage);
@@ -662,9 +720,9 @@ struct Epilogue {
       }
     }
     if (full)
-      store_kind<false, true, SB>(a, tk, acc, wm, wn, stage);
+      store_kind<false, true, SB, ADD>(a, tk, acc, wm, wn, stage);
     else
-      store_kind<false, false, SB>(a, tk, acc, wm, wn, stage);
+      store_kind<false, false, SB, ADD>(a, tk, acc, wm, wn, stage);
   }
 
 };

@@ -22,6 +22,7 @@ struct Instance {
   LaunchFn launch;
   int threads;
   int bk;
+  bool add = false;  // matmul-add epilogue (C = A.B + X)
 };
 
 struct InstanceList {
@@ -35,9 +36,9 @@ hipError_t launch_reg(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
   return hipGetLastError();
 }
 
-template <int AB, int BM, int BN, int WM, int WN, int S, bool GR>
+template <int AB, int BM, int BN, int WM, int WN, int S, bool GR, bool ADD = false>
 hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
-  hipLaunchKernelGGL((gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR, ADD>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -52,6 +53,14 @@ hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
     AB, BM, BN, GR, true, S,                                                              \
         reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR>),       \
         &launch_dma<AB, BM, BN, WM, WN, S, GR>, 64 * WM * WN, Traits<AB>::BK              \
+  }
+
+// A matmul-add instance of the LDS-DMA family (plain GEMM only).
+#define BST_DMA_ADD(AB, BM, BN, WM, WN, S)                                                \
+  Instance {                                                                              \
+    AB, BM, BN, false, true, S,                                                           \
+        reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, false, true>), \
+        &launch_dma<AB, BM, BN, WM, WN, S, false, true>, 64 * WM * WN, Traits<AB>::BK, true \
   }
 
 InstanceList instances_f16();

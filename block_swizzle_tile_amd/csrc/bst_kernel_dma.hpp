@@ -188,7 +188,7 @@ struct LoopTrace {
 // chunk blocks inside which a B row is permuted.
 constexpr int pow2_block(int n) { return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1; }
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, bool ADD = false>
 struct DmaKernel {
   using T = Traits<AB>;
   using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
@@ -744,7 +744,8 @@ struct DmaKernel {
     uint64_t t_fix = t_epi;
     if (Epi::fixup(a, acc, s, t)) {
       t_fix = trace_stamp();
-      Epi::template store_tile<STAGE_BYTES>(a, tk, acc, wm, wn, stage_buf<0, STAGE_BYTES>());
+      Epi::template store_tile<STAGE_BYTES, ADD>(a, tk, acc, wm, wn,
+                                                 stage_buf<0, STAGE_BYTES>());
     }
 #ifdef BST_TRACE
     const uint64_t t_end = trace_stamp();
@@ -855,10 +856,11 @@ struct DmaKernel {
   }
 };
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+// ADD: the matmul-add instances (C = A.B + X; plain GEMM only).
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, bool ADD = false>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only builtins: device pass only
-  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>::run(a);
+  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED, ADD>::run(a);
 #endif
 }
 

@@ -14,6 +14,7 @@ static const Instance kList[] = {
     BST_DMA(AB_BF16, 128, 192, 2, 2, 3, false), BST_DMA(AB_BF16, 128, 128, 2, 2, 4, true),
     BST_DMA(AB_BF16, 256, 256, 4, 2, 2, false),
     BST_DMA(AB_BF16, 128, 64, 2, 2, 4, false),  BST_DMA(AB_BF16, 64, 128, 2, 2, 4, false),
+    BST_DMA_ADD(AB_BF16, 64, 64, 2, 2, 4), BST_DMA_ADD(AB_BF16, 128, 128, 2, 2, 4),
 };
 
 InstanceList instances_bf16() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }

@@ -12,6 +12,7 @@ static const Instance kList[] = {
     BST_DMA(AB_I8, 256, 128, 2, 2, 3, false),  BST_DMA(AB_I8, 256, 256, 4, 2, 2, false),
     BST_DMA(AB_I8, 64, 64, 2, 2, 4, true),     BST_DMA(AB_I8, 128, 128, 2, 2, 4, true),
     BST_DMA(AB_I8, 256, 128, 2, 2, 3, true),   BST_DMA(AB_I8, 256, 256, 4, 2, 2, true),
+    BST_DMA_ADD(AB_I8, 128, 128, 2, 2, 4),
 };
 
 InstanceList instances_i8() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }

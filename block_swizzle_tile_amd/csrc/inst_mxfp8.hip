@@ -10,6 +10,7 @@ static const Instance kList[] = {
     BST_DMA(AB_MXE4M3, 64, 64, 2, 2, 4, false),  BST_DMA(AB_MXE4M3, 128, 128, 2, 2, 4, false),
     BST_DMA(AB_MXE4M3, 256, 128, 2, 2, 3, false), BST_DMA(AB_MXE4M3, 256, 256, 4, 2, 2, false),
     BST_DMA(AB_MXE4M3, 128, 64, 2, 2, 4, false),  BST_DMA(AB_MXE4M3, 64, 128, 2, 2, 4, false),
+    BST_DMA_ADD(AB_MXE4M3, 64, 128, 2, 2, 4), BST_DMA_ADD(AB_MXE4M3, 128, 128, 2, 2, 4),
 };
 
 InstanceList instances_mxfp8() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }

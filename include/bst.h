@@ -114,6 +114,22 @@ bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
                     size_t ws_bytes, void* stream);
 
 /*
+ * bst_gemm_add -- C = A . B + X (the matmul-add example that "Block Dispatch
+ * Policies" lists under its ping-pong policy; reading: X has C's shape and
+ * dtype c).  Same operands, scales, schedule and workspace as bst_gemm.
+ *   X_dev: [M][ldx] of dtype c, 16-byte aligned, ldx >= N with ldx * sizeof
+ *   a 16-byte multiple; it may be C itself (C += A . B).  Each output adds
+ *   X in fp32 (int32 for BST_I32, wrapping) to the fp32 accumulator and is
+ *   rounded once.  Errors as bst_gemm, plus BST_E_INVAL for a NULL X or a
+ *   small ldx and BST_E_ALIGN for a misaligned X.
+ */
+bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                        const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
+                        const void* X_dev, int64_t ldx, void* C_dev, int64_t ldc,
+                        const uint8_t* scale_a_dev, const uint8_t* scale_b_dev,
+                        const bst_sched* sched, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * bst_batched_gemm -- C_b = A_b . B_b for b in [0, batch), with
  * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in
  * elements).  The task index spans batch x tiles; the batch index of task t

@@ -121,6 +121,24 @@ def test_effective_sched_split_resolution(L):
                                  ctypes.byref(out)) == _lib.E_INVAL
 
 
+def test_gemm_add_validation(L):
+    """bst_gemm_add (C = A.B + X): validation before any launch."""
+    def add(X=FAKE, ldx=64, sched=None, **kw):
+        a = dict(ab=_lib.F16, c=_lib.F16, M=64, N=64, K=64, A=FAKE, lda=64, B=FAKE, ldb=64,
+                 C=FAKE2, ldc=64)
+        a.update(kw)
+        return L.bst_gemm_add(a["ab"], a["c"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                              a["B"], a["ldb"], X, ldx, a["C"], a["ldc"], None, None,
+                              None if sched is None else ctypes.byref(sched), None, 0, None)
+    assert add(X=None) == _lib.E_INVAL                       # the addend is required
+    assert add(ldx=32) == _lib.E_INVAL                       # ldx < N
+    assert add(X=ODD) == _lib.E_ALIGN
+    assert add(ldx=68) == _lib.E_ALIGN                       # 136-byte rows
+    assert add(sched=S(tile=(256, 128))) == _lib.E_UNSUPPORTED   # no matmul-add instance
+    assert add(sched=S(tile=(64, 64), path=1)) == _lib.E_UNSUPPORTED  # LDS-DMA family only
+    assert add(M=0, X=None) == _lib.OK                        # empty: nothing to add
+
+
 def test_effective_sched_shuffle_k(L):
     """ShuffleK is applied by the LDS-DMA family only; the register-staged one runs stages in
     order and reports 0."""
