@@ -226,8 +226,15 @@ def all_configs(args, bst, I, gpu, torch):
     f2 = 2.0 * w["M"] * w["N"] * w["K"]
     for kw in (dict(tile=(256, 128), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(256, 128), offset=4, direction="zn", xcd_remap=0),
-               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1)):
+               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1),
+               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1)):
         run("C2 fp16 1024x1024x2048", f2, "f16", kw, lambda s: bst.gemm(A, B, C, sched=s))
+
+    # matmul-add on the same workload: C = A.B + X with a seeded fp16 addend
+    X = gpu(I.uniform_f16((w["M"], w["N"]), I.WORKLOAD_IDS["fp16_2k"], 7, -4.0, 4.0), "f16")
+    run("C2 fp16 1024x1024x2048 matmul-add (+X)", f2, "f16",
+        dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1),
+        lambda s: bst.gemm(A, B, C, sched=s, add=X))
 
     x = I.workload("mxfp8_4k")
     Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
