@@ -22,7 +22,7 @@ from ._lib import (BF16, E4M3, F16, F32, I8, I32, MXE4M3, BstError, Sched, check
 ZN, NZ, RASTER = 0, 1, 2
 _DIRS = {"zn": ZN, "nz": NZ, "raster": RASTER}
 
-__all__ = ["Sched", "BstError", "make_sched", "gemm", "batched_gemm", "grouped_gemm_slice_m",
+__all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_gemm", "grouped_gemm_slice_m",
            "quant_gemm_per_token", "tile_map", "grouped_tile_map", "workspace_bytes",
            "effective_sched", "version", "LIB_PATH"]
 
@@ -35,6 +35,32 @@ def make_sched(tile=(0, 0), tile_k=0, offset=1, direction="zn", split_k=1, xcd_r
     d = _DIRS[direction] if isinstance(direction, str) else int(direction)
     return Sched(tile[0], tile[1], tile_k, offset, d, split_k, xcd_remap, grid, path,
                  int(shuffle_k))
+
+
+def gemm_padded(A, B, C=None, *, out_dtype=None, scale_a=None, scale_b=None, sched=None,
+                workspace=None):
+    """C = A @ B for operands with any row stride and element-aligned base (e.g. column
+    slices): they are repacked into an aligned workspace first (bst_gemm_padded)."""
+    torch = _torch()
+    _dev(A, B, C, scale_a, scale_b)
+    scaled = scale_a is not None
+    ab = _code(A.dtype, scaled)
+    if _code(B.dtype, scaled) != ab:
+        raise TypeError("A and B dtypes differ")
+    M, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        if out_dtype is None:
+            out_dtype = {F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.bfloat16,
+                         MXE4M3: torch.bfloat16, I8: torch.int32}[ab]
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    c = _code(C.dtype)
+    nb = workspace_bytes(2, ab, 1, M, N, K, sched)
+    ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(nb, A.device)
+    check(lib().bst_gemm_padded(ab, c, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C),
+                                _ld(C), _ptr(scale_a), _ptr(scale_b), _sched(sched), _ptr(ws),
+                                wsb, _stream(A.device)))
+    return C
 
 
 def version():

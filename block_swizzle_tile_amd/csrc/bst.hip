@@ -345,6 +345,61 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   return launch(p, a, stream);
 }
 
+// ------------------------------------------------------- padding GEMM ----
+// Row repack of an operand into the workspace: dst[r][c] = src[r][c] for
+// c < cols and 0 for cols <= c < dld, rows x dld elements.  Reads stay inside
+// the caller's rows x cols matrix, writes inside rows x dld.
+template <typename E>
+__global__ void repack_kernel(const E* __restrict__ src, int64_t sld, E* __restrict__ dst,
+                              int64_t dld, int64_t rows, int64_t cols) {
+  const int64_t total = rows * dld;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
+    const int64_t r = i / dld, c = i - r * dld;
+    dst[i] = c < cols ? src[r * sld + c] : E(0);
+  }
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Repacked leading dimensions (whole 16-byte rows) and the bytes both
+// repacked operands take, each at a 256-byte boundary.
+struct Padded {
+  int64_t lda = 0, ldb = 0;
+  size_t a_bytes = 0, bytes = 0;
+};
+Padded padded_layout(bst_dtype ab, int64_t M, int64_t N, int64_t K) {
+  Padded q;
+  const int64_t es = (int64_t)elem_size(ab), ce = 16 / es;
+  q.lda = round_up(K, ce);
+  q.ldb = round_up(N, ce);
+  q.a_bytes = (size_t)round_up(M * q.lda * es, 256);
+  q.bytes = q.a_bytes + (size_t)round_up(K * q.ldb * es, 256);
+  return q;
+}
+
+size_t padded_gemm_ws(const Plan& p) {
+  return (size_t)round_up((int64_t)std::max(p.ws_bytes, kCounterBytes), 256);
+}
+
+bst_status repack(bst_dtype ab, const void* src, int64_t sld, void* dst, int64_t dld, int64_t rows,
+                  int64_t cols, void* stream) {
+  const int64_t total = rows * dld;
+  if (total == 0) return BST_OK;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  if (elem_size(ab) == 2)
+    hipLaunchKernelGGL((repack_kernel<uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, static_cast<const uint16_t*>(src), sld,
+                       static_cast<uint16_t*>(dst), dld, rows, cols);
+  else
+    hipLaunchKernelGGL((repack_kernel<uint8_t>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, static_cast<const uint8_t*>(src), sld,
+                       static_cast<uint8_t*>(dst), dld, rows, cols);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BST_E_HIP, "repack launch failed: %s", hipGetErrorString(e));
+  return BST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,6 +431,45 @@ bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t
   if (M > 0 && N > 0 && !X) return fail(BST_E_INVAL, "the addend X is NULL");
   return dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
                nullptr, s, ws, ws_bytes, stream, X, ldx);
+}
+
+bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                           int64_t ldc, const uint8_t* scale_a, const uint8_t* scale_b,
+                           const bst_sched* s, void* ws, size_t ws_bytes, void* stream) {
+  if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
+  if (ab != BST_MXE4M3 && (scale_a || scale_b))
+    return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
+  if (M < 0 || N < 0 || K < 0) return fail(BST_E_INVAL, "negative size");
+  if (M == 0 || N == 0) return BST_OK;
+  if (K > 0 && (!A || !B)) return fail(BST_E_INVAL, "A or B is NULL");
+  if (K > 0 && (lda < K || ldb < N))
+    return fail(BST_E_INVAL, "leading dimension too small (lda %lld K %lld, ldb %lld N %lld)",
+                (long long)lda, (long long)K, (long long)ldb, (long long)N);
+  const Padded q = padded_layout(ab, M, N, K);
+  Plan p;
+  const Layout lay{q.lda, q.ldb, scale_a, scale_b};
+  bst_status st = make_plan(0, ab, 1, M, N, K, s, true, p, &lay);
+  if (st != BST_OK) return st;
+  // The GEMM's own workspace comes first, its split-K counters at offset 0
+  // whatever the split, so that a workspace shared with other calls keeps
+  // its counter area zero; the repacked operands follow.
+  const size_t gws = padded_gemm_ws(p);
+  if (!ws || ws_bytes < gws + q.bytes)
+    return fail(BST_E_WORKSPACE, "the padding GEMM needs %zu workspace bytes (got %zu)",
+                gws + q.bytes, ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BST_E_ALIGN, "workspace not 16-byte aligned");
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint8_t* ap = w + gws;
+  uint8_t* bp = ap + q.a_bytes;
+  if (K > 0) {
+    st = repack(ab, A, lda, ap, q.lda, M, K, stream);
+    if (st != BST_OK) return st;
+    st = repack(ab, B, ldb, bp, q.ldb, K, N, stream);
+    if (st != BST_OK) return st;
+  }
+  return dense(ab, c, 1, M, N, K, ap, q.lda, 0, bp, q.ldb, 0, C, ldc, 0, scale_a, scale_b,
+               nullptr, nullptr, s, w, gws, stream);
 }
 
 bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
@@ -520,9 +614,16 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
 size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
                            const bst_sched* s) {
   Plan p;
-  if (kind != 0 && kind != 1) {
-    fail(BST_E_INVAL, "kind must be 0 or 1");
+  if (kind < 0 || kind > 2) {
+    fail(BST_E_INVAL, "kind must be 0, 1 or 2");
     return 0;
+  }
+  if (kind == 2) {  // bst_gemm_padded: the repacked operands, then the split-K workspace
+    if (!is_ab(ab) || M < 0 || N < 0 || K < 0) return 0;
+    const Padded q = padded_layout(ab, M, N, K);
+    const Layout lay{q.lda, q.ldb, nullptr, nullptr};
+    if (make_plan(0, ab, 1, M, N, K, s, true, p, &lay) != BST_OK) return 0;
+    return padded_gemm_ws(p) + q.bytes;
   }
   if (make_plan(kind, ab, count, M, N, K, s, true, p) != BST_OK) return 0;
   return p.ws_bytes;

@@ -130,6 +130,26 @@ bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t
                         const bst_sched* sched, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bst_gemm_padded -- bst_gemm for operands whose rows are not whole 16-byte
+ * chunks or whose base is not 16-byte aligned (the padding matmul example
+ * that "Block Dispatch Policies" lists under its ping-pong policy; reading:
+ * repack the operands into an aligned, zero-padded layout, then run the
+ * GEMM).  A [M][lda] and B [K][ldb] may have any leading dimension >= K / N
+ * and any element-aligned base; the call copies them into the workspace
+ * with rows rounded up to whole 16-byte chunks (zeros in the padding) and
+ * runs bst_gemm on the copies, in stream order.  C, the MX scales and the
+ * rest are as for bst_gemm (C stays 16-byte aligned).  ws: at least
+ * bst_workspace_bytes(2, ab, 1, M, N, K, sched) bytes, 16-byte aligned
+ * (BST_E_WORKSPACE / BST_E_ALIGN otherwise); the call owns it until the
+ * GEMM has run.
+ */
+bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                           const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
+                           void* C_dev, int64_t ldc, const uint8_t* scale_a_dev,
+                           const uint8_t* scale_b_dev, const bst_sched* sched, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * bst_batched_gemm -- C_b = A_b . B_b for b in [0, batch), with
  * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in
  * elements).  The task index spans batch x tiles; the batch index of task t
@@ -208,8 +228,9 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m_
 /*
  * bst_workspace_bytes -- workspace bytes a call with these arguments needs
  * (0 when the effective split_k is 1).  kind: 0 plain / batched (count =
- * batch), 1 grouped (count = G, M = total_m).  Returns 0 and sets the last
- * error for invalid arguments.
+ * batch), 1 grouped (count = G, M = total_m), 2 bst_gemm_padded (count 1;
+ * the repacked operands plus the split-K workspace, never 0 for a non-empty
+ * problem).  Returns 0 and sets the last error for invalid arguments.
  */
 size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                            int64_t K, const bst_sched* sched);

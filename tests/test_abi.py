@@ -139,6 +139,27 @@ def test_gemm_add_validation(L):
     assert add(M=0, X=None) == _lib.OK                        # empty: nothing to add
 
 
+def test_gemm_padded_validation(L):
+    """bst_gemm_padded: workspace sizing and validation before any launch."""
+    need = L.bst_workspace_bytes(2, _lib.F16, 1, 64, 64, 60, None)
+    # 64 KiB counter area, then A 64 x 64 and B 60 x 64 fp16 rows padded to 16 bytes
+    assert need == 65536 + 64 * 64 * 2 + 60 * 64 * 2
+    assert L.bst_workspace_bytes(3, _lib.F16, 1, 64, 64, 60, None) == 0   # no such kind
+
+    def pad(ws=None, wsb=0, **kw):
+        a = dict(M=64, N=64, K=60, A=ODD, lda=61, B=ODD, ldb=67, C=FAKE2, ldc=64)
+        a.update(kw)
+        return L.bst_gemm_padded(_lib.F16, _lib.F16, a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                 a["B"], a["ldb"], a["C"], a["ldc"], None, None, None, ws, wsb,
+                                 None)
+    assert pad() == _lib.E_WORKSPACE                          # odd strides are fine, ws is not
+    assert pad(ws=FAKE, wsb=need - 1) == _lib.E_WORKSPACE
+    assert pad(ws=ODD, wsb=need) == _lib.E_ALIGN
+    assert pad(lda=59) == _lib.E_INVAL                        # lda < K
+    assert pad(A=None) == _lib.E_INVAL
+    assert pad(M=0) == _lib.OK
+
+
 def test_effective_sched_shuffle_k(L):
     """ShuffleK is applied by the LDS-DMA family only; the register-staged one runs stages in
     order and reports 0."""
