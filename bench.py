@@ -236,6 +236,17 @@ def all_configs(args, bst, I, gpu, torch):
         dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1),
         lambda s: bst.gemm(A, B, C, sched=s, add=X))
 
+    # padding matmul on the same workload, with operands whose rows are 2 bytes longer
+    # (odd strides): repacked into the workspace, then multiplied
+    Ao = torch.zeros((w["M"], w["K"] + 1), dtype=torch.float16, device="cuda")
+    Bo = torch.zeros((w["K"], w["N"] + 1), dtype=torch.float16, device="cuda")
+    Ao[:, :w["K"]] = A
+    Bo[:, :w["N"]] = B
+    Ao, Bo = Ao[:, :w["K"]], Bo[:, :w["N"]]
+    run("C2 fp16 1024x1024x2048 padding matmul (odd strides)", f2, "f16",
+        dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1),
+        lambda s: bst.gemm_padded(Ao, Bo, C, sched=s))
+
     x = I.workload("mxfp8_4k")
     Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
     sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
