@@ -349,14 +349,15 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
 // Row repack of an operand into the workspace: dst[r][c] = src[r][c] for
 // c < cols and 0 for cols <= c < dld, rows x dld elements.  Reads stay inside
 // the caller's rows x cols matrix, writes inside rows x dld.
+// One workgroup per row at a time (rows strided over the grid), its threads
+// over the row's elements, so that loads and stores are consecutive.
 template <typename E>
 __global__ void repack_kernel(const E* __restrict__ src, int64_t sld, E* __restrict__ dst,
                               int64_t dld, int64_t rows, int64_t cols) {
-  const int64_t total = rows * dld;
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
-    const int64_t r = i / dld, c = i - r * dld;
-    dst[i] = c < cols ? src[r * sld + c] : E(0);
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const E* s = src + r * sld;
+    E* d = dst + r * dld;
+    for (int64_t c = threadIdx.x; c < dld; c += blockDim.x) d[c] = c < cols ? s[c] : E(0);
   }
 }
 
@@ -384,9 +385,8 @@ size_t padded_gemm_ws(const Plan& p) {
 
 bst_status repack(bst_dtype ab, const void* src, int64_t sld, void* dst, int64_t dld, int64_t rows,
                   int64_t cols, void* stream) {
-  const int64_t total = rows * dld;
-  if (total == 0) return BST_OK;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  if (rows * dld == 0) return BST_OK;
+  const int64_t blocks = std::min<int64_t>(rows, 4096);
   if (elem_size(ab) == 2)
     hipLaunchKernelGGL((repack_kernel<uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)stream, static_cast<const uint16_t*>(src), sld,
