@@ -121,7 +121,10 @@ bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
  *   a 16-byte multiple; it may be C itself (C += A . B).  Each output adds
  *   X in fp32 (int32 for BST_I32, wrapping) to the fp32 accumulator and is
  *   rounded once.  Errors as bst_gemm, plus BST_E_INVAL for a NULL X or a
- *   small ldx and BST_E_ALIGN for a misaligned X.
+ *   small ldx, BST_E_ALIGN for a misaligned X, and BST_E_UNSUPPORTED for a
+ *   tile without a matmul-add kernel (fp16 / bf16: 64x64, 128x128; MX-fp8:
+ *   64x128, 128x128; fp8 and int8: 128x128) or for operands the LDS-DMA
+ *   kernels cannot take (K or N not in whole 16-byte chunks, path 1).
  */
 bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
                         const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
