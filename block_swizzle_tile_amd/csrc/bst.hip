@@ -350,14 +350,28 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
 // c < cols and 0 for cols <= c < dld, rows x dld elements.  Reads stay inside
 // the caller's rows x cols matrix, writes inside rows x dld.
 // One workgroup per row at a time (rows strided over the grid), its threads
-// over the row's elements, so that loads and stores are consecutive.
+// over the row's elements, so that loads and stores are consecutive; each
+// thread keeps four loads in flight before it stores.
 template <typename E>
 __global__ void repack_kernel(const E* __restrict__ src, int64_t sld, E* __restrict__ dst,
                               int64_t dld, int64_t rows, int64_t cols) {
+  const int64_t nt = blockDim.x;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const E* s = src + r * sld;
     E* d = dst + r * dld;
-    for (int64_t c = threadIdx.x; c < dld; c += blockDim.x) d[c] = c < cols ? s[c] : E(0);
+    for (int64_t c0 = threadIdx.x; c0 < dld; c0 += 4 * nt) {
+      E v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + u * nt;
+        v[u] = c < cols ? s[c] : E(0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + u * nt;
+        if (c < dld) d[c] = v[u];
+      }
+    }
   }
 }
 
