@@ -24,7 +24,7 @@ _DIRS = {"zn": ZN, "nz": NZ, "raster": RASTER}
 
 __all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_gemm", "grouped_gemm_slice_m",
            "quant_gemm_per_token", "tile_map", "grouped_tile_map", "workspace_bytes",
-           "effective_sched", "version", "LIB_PATH"]
+           "effective_sched", "task_count", "version", "LIB_PATH"]
 
 
 def make_sched(tile=(0, 0), tile_k=0, offset=1, direction="zn", split_k=1, xcd_remap=0, grid=0,
@@ -241,12 +241,19 @@ def quant_gemm_per_token(A, B, row_scale, col_scale, C=None, *, out_dtype=None, 
     return C
 
 
+def task_count(kind, ab, count, M, N, sched=None):
+    """Task count of the scheduler (kind 0: exact, count = batch; kind 1: the bound for a
+    grouped problem, count = G, M = total_m)."""
+    n = ctypes.c_int64(0)
+    check(lib().bst_task_count(kind, ab, count, M, N, _sched(sched), ctypes.byref(n)))
+    return n.value
+
+
 def tile_map(batch, M, N, sched=None, *, ab=F16, device="cuda"):
     """[T, 8] int32 tensor of {batch, m, n, mActual, nActual, 0, xcc, workgroup} per task,
     computed on the GPU by the kernels' scheduler."""
     torch = _torch()
-    s = effective_sched(0, ab, batch, M, N, 0, sched)
-    T = batch * (-(-M // s.tile_m)) * (-(-N // s.tile_n))
+    T = task_count(0, ab, batch, M, N, sched)
     out = torch.full((max(T, 1), 8), -1, dtype=torch.int32, device=device)
     check(lib().bst_tile_map(ab, batch, M, N, _sched(sched), _ptr(out), out.shape[0],
                              _stream(out.device)))
@@ -259,8 +266,7 @@ def grouped_tile_map(group_m, total_m, N, sched=None, *, ab=I8):
     torch = _torch()
     _dev(group_m)
     G = group_m.numel()
-    s = effective_sched(1, ab, G, total_m, N, 0, sched)
-    bound = ((-(-total_m // s.tile_m)) + G) * (-(-N // s.tile_n))
+    bound = task_count(1, ab, G, total_m, N, sched)
     out = torch.full((max(bound, 1), 8), -1, dtype=torch.int32, device=group_m.device)
     check(lib().bst_grouped_tile_map(ab, G, _ptr(group_m), total_m, N, _sched(sched), _ptr(out),
                                      out.shape[0], _stream(group_m.device)))

@@ -22,7 +22,7 @@ F16, BF16, E4M3, MXE4M3, I8, I32, F32 = 1, 2, 3, 4, 5, 6, 7
 
 EXPORTS = ["bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm", "bst_grouped_gemm_slice_m", "bst_quant_gemm_per_token",
            "bst_tile_map", "bst_grouped_tile_map", "bst_workspace_bytes", "bst_effective_sched",
-           "bst_last_error", "bst_version"]
+           "bst_task_count", "bst_last_error", "bst_version"]
 
 
 class Sched(ctypes.Structure):
@@ -61,9 +61,11 @@ def lib():
             L.bst_workspace_bytes.argtypes = [ctypes.c_int, st, i64, i64, i64, i64, sp]
             L.bst_workspace_bytes.restype = sz
             L.bst_effective_sched.argtypes = [ctypes.c_int, st, i64, i64, i64, i64, sp, sp]
+            L.bst_task_count.argtypes = [ctypes.c_int, st, i64, i64, i64, sp,
+                                         ctypes.POINTER(i64)]
             for fn in ("bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm", "bst_grouped_gemm_slice_m",
                        "bst_quant_gemm_per_token", "bst_tile_map", "bst_grouped_tile_map",
-                       "bst_effective_sched"):
+                       "bst_effective_sched", "bst_task_count"):
                 getattr(L, fn).restype = st
             L.bst_last_error.restype = ctypes.c_char_p
             L.bst_version.restype = ctypes.c_char_p

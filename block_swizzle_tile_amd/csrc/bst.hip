@@ -277,16 +277,19 @@ bst_status launch(const Plan& p, const GemmArgs& a, void* stream) {
   return BST_OK;
 }
 
-// Shared by gemm and batched_gemm.
-bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N, int64_t K,
-                 const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
-                 int64_t strideB, void* C, int64_t ldc, int64_t strideC, const uint8_t* sa,
-                 const uint8_t* sb, const float* rs, const float* cs, const bst_sched* s,
-                 void* ws, size_t ws_bytes, void* stream, const void* X = nullptr,
-                 int64_t ldx = 0) {
+// Validation and set-up shared by gemm, gemm_add, gemm_padded and
+// batched_gemm: checks every argument, resolves the plan and fills the
+// kernel arguments, and enqueues nothing.  On BST_OK, `empty` tells that the
+// problem has no output (nothing to launch).
+bst_status prepare_dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
+                         int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B,
+                         int64_t ldb, int64_t strideB, void* C, int64_t ldc, int64_t strideC,
+                         const uint8_t* sa, const uint8_t* sb, const float* rs, const float* cs,
+                         const bst_sched* s, void* ws, size_t ws_bytes, const void* X,
+                         int64_t ldx, Plan& p, GemmArgs& a, bool& empty) {
+  empty = true;
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
-  Plan p;
   bst_status st = make_plan(0, ab, batch, M, N, K, s, false, p, nullptr, X != nullptr);
   if (st != BST_OK) return st;
   if (batch == 0 || M == 0 || N == 0) return BST_OK;
@@ -299,6 +302,11 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
                 (long long)lda, (long long)K, (long long)ldb, (long long)N, (long long)ldc);
   if (batch > 1 && (strideA < 0 || strideB < 0 || strideC < 0))
     return fail(BST_E_INVAL, "negative batch stride");
+  // batches of C must not overlap (their tasks run concurrently); A and B
+  // are only read, so theirs may
+  if (batch > 1 && strideC < (M - 1) * ldc + N)
+    return fail(BST_E_INVAL, "strideC %lld lets batches of C overlap (need >= %lld)",
+                (long long)strideC, (long long)((M - 1) * ldc + N));
   if (ab == BST_MXE4M3 && has_k && (!sa || !sb)) return fail(BST_E_INVAL, "MX scales are NULL");
   if ((rs == nullptr) != (cs == nullptr)) return fail(BST_E_INVAL, "give both dequant scales or neither");
   if (X && (batch != 1 || rs)) return fail(BST_E_INVAL, "the addend is taken by bst_gemm_add only");
@@ -317,7 +325,7 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
 
-  GemmArgs a{};
+  a = GemmArgs{};
 #ifdef BST_TRACE
   a.trace = g_trace;
 #endif
@@ -342,29 +350,48 @@ bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
   a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
+  empty = false;
+  return BST_OK;
+}
+
+bst_status dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                 int64_t strideB, void* C, int64_t ldc, int64_t strideC, const uint8_t* sa,
+                 const uint8_t* sb, const float* rs, const float* cs, const bst_sched* s,
+                 void* ws, size_t ws_bytes, void* stream, const void* X = nullptr,
+                 int64_t ldx = 0) {
+  Plan p;
+  GemmArgs a{};
+  bool empty = true;
+  const bst_status st = prepare_dense(ab, c, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C,
+                                      ldc, strideC, sa, sb, rs, cs, s, ws, ws_bytes, X, ldx, p, a,
+                                      empty);
+  if (st != BST_OK || empty) return st;
   return launch(p, a, stream);
 }
 
 // ------------------------------------------------------- padding GEMM ----
 // Row repack of an operand into the workspace: dst[r][c] = src[r][c] for
-// c < cols and 0 for cols <= c < dld, rows x dld elements.  Reads stay inside
-// the caller's rows x cols matrix, writes inside rows x dld.
+// r < rows and c < cols, 0 elsewhere in drows x dld elements (drows >= rows).
+// Reads stay inside the caller's rows x cols matrix, writes inside
+// drows x dld.
 // One workgroup per row at a time (rows strided over the grid), its threads
 // over the row's elements, so that loads and stores are consecutive; each
 // thread keeps four loads in flight before it stores.
 template <typename E>
 __global__ void repack_kernel(const E* __restrict__ src, int64_t sld, E* __restrict__ dst,
-                              int64_t dld, int64_t rows, int64_t cols) {
+                              int64_t dld, int64_t rows, int64_t cols, int64_t drows) {
   const int64_t nt = blockDim.x;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const E* s = src + r * sld;
+  for (int64_t r = blockIdx.x; r < drows; r += gridDim.x) {
+    const bool live = r < rows;  // rows past the source are all zeros
+    const E* s = src + (live ? r : 0) * sld;
     E* d = dst + r * dld;
     for (int64_t c0 = threadIdx.x; c0 < dld; c0 += 4 * nt) {
       E v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int64_t c = c0 + u * nt;
-        v[u] = c < cols ? s[c] : E(0);
+        v[u] = (live && c < cols) ? s[c] : E(0);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -377,10 +404,14 @@ __global__ void repack_kernel(const E* __restrict__ src, int64_t sld, E* __restr
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Repacked leading dimensions (whole 16-byte rows) and the bytes both
-// repacked operands take, each at a 256-byte boundary.
+// Repacked layout: A as [M][lda] and B as [kp][ldb] with rows of whole
+// 16-byte chunks, zeros in the padding; the GEMM then runs with K = kp (A's
+// padding columns meet B's zero rows, so every added product is an exact 0),
+// which lets the LDS-DMA kernels take it whatever K was.  The int8 bound on
+// K is kept: kp stays K when padding would cross it.  Both copies start at a
+// 256-byte boundary.
 struct Padded {
-  int64_t lda = 0, ldb = 0;
+  int64_t lda = 0, ldb = 0, kp = 0;
   size_t a_bytes = 0, bytes = 0;
 };
 Padded padded_layout(bst_dtype ab, int64_t M, int64_t N, int64_t K) {
@@ -388,8 +419,9 @@ Padded padded_layout(bst_dtype ab, int64_t M, int64_t N, int64_t K) {
   const int64_t es = (int64_t)elem_size(ab), ce = 16 / es;
   q.lda = round_up(K, ce);
   q.ldb = round_up(N, ce);
+  q.kp = (ab == BST_I8 && q.lda > 131071) ? K : q.lda;
   q.a_bytes = (size_t)round_up(M * q.lda * es, 256);
-  q.bytes = q.a_bytes + (size_t)round_up(K * q.ldb * es, 256);
+  q.bytes = q.a_bytes + (size_t)round_up(q.kp * q.ldb * es, 256);
   return q;
 }
 
@@ -398,17 +430,17 @@ size_t padded_gemm_ws(const Plan& p) {
 }
 
 bst_status repack(bst_dtype ab, const void* src, int64_t sld, void* dst, int64_t dld, int64_t rows,
-                  int64_t cols, void* stream) {
-  if (rows * dld == 0) return BST_OK;
-  const int64_t blocks = std::min<int64_t>(rows, 4096);
+                  int64_t cols, int64_t drows, void* stream) {
+  if (drows * dld == 0) return BST_OK;
+  const int64_t blocks = std::min<int64_t>(drows, 4096);
   if (elem_size(ab) == 2)
     hipLaunchKernelGGL((repack_kernel<uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)stream, static_cast<const uint16_t*>(src), sld,
-                       static_cast<uint16_t*>(dst), dld, rows, cols);
+                       static_cast<uint16_t*>(dst), dld, rows, cols, drows);
   else
     hipLaunchKernelGGL((repack_kernel<uint8_t>), dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)stream, static_cast<const uint8_t*>(src), sld,
-                       static_cast<uint8_t*>(dst), dld, rows, cols);
+                       static_cast<uint8_t*>(dst), dld, rows, cols, drows);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BST_E_HIP, "repack launch failed: %s", hipGetErrorString(e));
   return BST_OK;
@@ -460,10 +492,14 @@ bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int6
   if (K > 0 && (lda < K || ldb < N))
     return fail(BST_E_INVAL, "leading dimension too small (lda %lld K %lld, ldb %lld N %lld)",
                 (long long)lda, (long long)K, (long long)ldb, (long long)N);
-  const Padded q = padded_layout(ab, M, N, K);
+  // the caller's K decides what is valid (MX blocks, the int8 bound); the
+  // GEMM then runs at the padded depth
   Plan p;
+  bst_status st = make_plan(0, ab, 1, M, N, K, s, false, p);
+  if (st != BST_OK) return st;
+  const Padded q = padded_layout(ab, M, N, K);
   const Layout lay{q.lda, q.ldb, scale_a, scale_b};
-  bst_status st = make_plan(0, ab, 1, M, N, K, s, true, p, &lay);
+  st = make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay);
   if (st != BST_OK) return st;
   // The GEMM's own workspace comes first, its split-K counters at offset 0
   // whatever the split, so that a workspace shared with other calls keeps
@@ -476,14 +512,20 @@ bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int6
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint8_t* ap = w + gws;
   uint8_t* bp = ap + q.a_bytes;
+  // every remaining check (output dtype, C, ldc, scales, workspace) before
+  // the first repack, so that a failing call has enqueued nothing
+  GemmArgs a{};
+  bool empty = true;
+  st = prepare_dense(ab, c, 1, M, N, q.kp, ap, q.lda, 0, bp, q.ldb, 0, C, ldc, 0, scale_a,
+                     scale_b, nullptr, nullptr, s, w, gws, nullptr, 0, p, a, empty);
+  if (st != BST_OK || empty) return st;
   if (K > 0) {
-    st = repack(ab, A, lda, ap, q.lda, M, K, stream);
+    st = repack(ab, A, lda, ap, q.lda, M, K, M, stream);
     if (st != BST_OK) return st;
-    st = repack(ab, B, ldb, bp, q.ldb, K, N, stream);
+    st = repack(ab, B, ldb, bp, q.ldb, K, N, q.kp, stream);
     if (st != BST_OK) return st;
   }
-  return dense(ab, c, 1, M, N, K, ap, q.lda, 0, bp, q.ldb, 0, C, ldc, 0, scale_a, scale_b,
-               nullptr, nullptr, s, w, gws, stream);
+  return launch(p, a, stream);
 }
 
 bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
@@ -632,11 +674,12 @@ size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int
     fail(BST_E_INVAL, "kind must be 0, 1 or 2");
     return 0;
   }
-  if (kind == 2) {  // bst_gemm_padded: the repacked operands, then the split-K workspace
+  if (kind == 2) {  // bst_gemm_padded: the split-K workspace, then the repacked operands
     if (!is_ab(ab) || M < 0 || N < 0 || K < 0) return 0;
+    if (make_plan(0, ab, 1, M, N, K, s, false, p) != BST_OK) return 0;
     const Padded q = padded_layout(ab, M, N, K);
     const Layout lay{q.lda, q.ldb, nullptr, nullptr};
-    if (make_plan(0, ab, 1, M, N, K, s, true, p, &lay) != BST_OK) return 0;
+    if (make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay) != BST_OK) return 0;
     return padded_gemm_ws(p) + q.bytes;
   }
   if (make_plan(kind, ab, count, M, N, K, s, true, p) != BST_OK) return 0;
@@ -646,10 +689,16 @@ size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int
 bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                                int64_t K, const bst_sched* s, bst_sched* out) {
   if (!out) return fail(BST_E_INVAL, "out is NULL");
-  if (kind != 0 && kind != 1) return fail(BST_E_INVAL, "kind must be 0 or 1");
+  if (kind < 0 || kind > 2) return fail(BST_E_INVAL, "kind must be 0, 1 or 2");
   Plan p;
-  const bst_status st = make_plan(kind, ab, count, M, N, K, s, true, p);
+  bst_status st = make_plan(kind == 2 ? 0 : kind, ab, count, M, N, K, s, true, p);
   if (st != BST_OK) return st;
+  if (kind == 2) {  // the GEMM bst_gemm_padded runs on the repacked operands
+    const Padded q = padded_layout(ab, M, N, K);
+    const Layout lay{q.lda, q.ldb, nullptr, nullptr};
+    st = make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay);
+    if (st != BST_OK) return st;
+  }
   out->tile_m = p.bm;
   out->tile_n = p.bn;
   out->tile_k = p.bk;
@@ -660,6 +709,20 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
   out->grid = p.grid;
   out->path = p.inst->dma ? 2u : 1u;
   out->shuffle_k = p.shuffle;
+  return BST_OK;
+}
+
+bst_status bst_task_count(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
+                          const bst_sched* s, int64_t* tasks) {
+  if (!tasks) return fail(BST_E_INVAL, "tasks is NULL");
+  if (kind != 0 && kind != 1) return fail(BST_E_INVAL, "kind must be 0 or 1");
+  bst_sched d{};
+  if (s) d = *s;
+  d.split_k = 1;
+  Plan p;
+  const bst_status st = make_plan(kind, ab, count, M, N, 0, s ? &d : nullptr, false, p);
+  if (st != BST_OK) return st;
+  *tasks = (int64_t)p.tile_cap;
   return BST_OK;
 }
 

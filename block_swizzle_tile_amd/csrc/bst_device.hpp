@@ -306,17 +306,6 @@ __device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
   return v;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
 // ---------------------------------------------------------------- kernel --
 // ------------------------------------------------------------ epilogue --
 // Shared by both kernel families: the fixed-order split-K fix-up and the

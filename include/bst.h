@@ -89,7 +89,12 @@ typedef struct bst_sched {
 } bst_sched;
 
 /*
- * bst_gemm -- C = A . B for one problem.
+ * bst_gemm -- C = A . B for one problem (the basic matmul that "Block
+ * Dispatch Policies" lists under its ping-pong policy), its output tiles
+ * visited in the order of the swizzled block scheduler ("Block Scheduler
+ * Code Explained", s4.3 GetCoreLoops for the task count, s4.5
+ * GetBlockCoord for each task's tile, s4.6 GetActualBlockShape for the tail
+ * tiles of the last tile-row and tile-column).
  *   ab: BST_F16 / BST_BF16 (c: BST_F16, BST_BF16 or BST_F32), BST_E4M3 /
  *   BST_MXE4M3 (c: BST_BF16, BST_F16 or BST_F32), BST_I8 (c: BST_I32 raw
  *   accumulators, or BST_F32 / BST_BF16 / BST_F16 of the accumulator).
@@ -139,12 +144,15 @@ bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t
  * repack the operands into an aligned, zero-padded layout, then run the
  * GEMM).  A [M][lda] and B [K][ldb] may have any leading dimension >= K / N
  * and any element-aligned base; the call copies them into the workspace
- * with rows rounded up to whole 16-byte chunks (zeros in the padding) and
- * runs bst_gemm on the copies, in stream order.  C, the MX scales and the
- * rest are as for bst_gemm (C stays 16-byte aligned).  ws: at least
- * bst_workspace_bytes(2, ab, 1, M, N, K, sched) bytes, 16-byte aligned
- * (BST_E_WORKSPACE / BST_E_ALIGN otherwise); the call owns it until the
- * GEMM has run.
+ * with rows rounded up to whole 16-byte chunks (zeros in the padding), B
+ * with K rounded up the same way (zero rows), and runs bst_gemm on the
+ * copies at that K, in stream order: the added products are exact zeros,
+ * and the copies fit the LDS-DMA kernels whenever N is a whole number of
+ * 16-byte chunks.  C, the MX scales and the rest are as for bst_gemm (C
+ * stays 16-byte aligned).  ws: at least bst_workspace_bytes(2, ab, 1, M,
+ * N, K, sched) bytes, 16-byte aligned (BST_E_WORKSPACE / BST_E_ALIGN
+ * otherwise); the call owns it until the GEMM has run.  Every argument is
+ * checked before the copies are enqueued.
  */
 bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
                            const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
@@ -157,7 +165,8 @@ bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int6
  * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in
  * elements).  The task index spans batch x tiles; the batch index of task t
  * is t / (tiles per problem) (s4.4 GetBatchIdx).  Same dtypes as bst_gemm
- * except BST_MXE4M3.
+ * except BST_MXE4M3.  With batch > 1 the batches of C may not overlap:
+ * strideC >= (M-1)*ldc + N (BST_E_INVAL otherwise); A and B batches may.
  */
 bst_status bst_batched_gemm(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, int64_t N,
                             int64_t K, const void* A_dev, int64_t lda, int64_t strideA,
@@ -191,7 +200,11 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G,
                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
- * bst_quant_gemm_per_token -- int8 A[M][K] . int8 B[K][N] with int32
+ * bst_quant_gemm_per_token -- the quantised matmul with per-token dequant
+ * ("Block Dispatch Policies" lists quant-matmul and per-token-dequant
+ * examples under its PreloadAsync policies; reading: one problem, the
+ * scales applied to the int32 accumulators in the epilogue):
+ * int8 A[M][K] . int8 B[K][N] with int32
  * accumulation and, for c = BST_BF16 / BST_F16 / BST_F32, the dequant
  * out = round(float(acc) * row_scale[i] * col_scale[j]) (row_scale f32 [M]
  * per token, col_scale f32 [N] per channel, both device pointers, both
@@ -206,7 +219,9 @@ bst_status bst_quant_gemm_per_token(int64_t M, int64_t N, int64_t K, const int8_
 
 /*
  * bst_tile_map -- the task -> tile map as the GPU computes it, with the
- * device scheduler the GEMM kernels use.  For every task t of a batched
+ * device scheduler the GEMM kernels use ("Block Scheduler Code Explained":
+ * s4.4 GetBatchIdx, s4.5 GetBlockCoord, s4.6 GetActualBlockShape, with the
+ * runtime offset and direction of s6).  For every task t of a batched
  * problem (batch x ceil(M/tile_m) x ceil(N/tile_n) tasks) writes 8 uint32
  * to out_dev[8t..8t+7]: {batch index, m, n, mActual, nActual, 0, XCC id of
  * the workgroup that ran it, that workgroup's index}.  `ab` selects the tile
@@ -239,9 +254,21 @@ size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int
                            int64_t K, const bst_sched* sched);
 
 /* bst_effective_sched -- fills *out with the schedule a call with these
- * arguments would run (defaults and automatic split resolved). */
+ * arguments would run (defaults and automatic split resolved).  kind as for
+ * bst_workspace_bytes (2: the GEMM bst_gemm_padded runs on its copies). */
 bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                                int64_t K, const bst_sched* sched, bst_sched* out);
+
+/* bst_task_count -- tasks of the block scheduler for these sizes (s4.3
+ * GetCoreLoops times the batch count, s4.4): kind 0 plain / batched
+ * (count = batch): exactly count * ceil(M/tile_m) * ceil(N/tile_n); kind 1
+ * grouped slice-M (count = G, M = total_m): the bound
+ * (ceil(total_m/tile_m) + G) * ceil(N/tile_n), since the group sizes live
+ * on the device.  This is the record count bst_tile_map /
+ * bst_grouped_tile_map need.  Tiles are the effective ones (defaults
+ * resolved). */
+bst_status bst_task_count(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
+                          const bst_sched* sched, int64_t* tasks);
 
 /* Message for the last non-OK status returned on this thread. */
 const char* bst_last_error(void);

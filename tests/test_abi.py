@@ -142,15 +142,16 @@ def test_gemm_add_validation(L):
 def test_gemm_padded_validation(L):
     """bst_gemm_padded: workspace sizing and validation before any launch."""
     need = L.bst_workspace_bytes(2, _lib.F16, 1, 64, 64, 60, None)
-    # 64 KiB counter area, then A 64 x 64 and B 60 x 64 fp16 rows padded to 16 bytes
-    assert need == 65536 + 64 * 64 * 2 + 60 * 64 * 2
+    # 64 KiB counter area, then A 64 x 64 and B 64 x 64 fp16: rows padded to 16 bytes and
+    # B's K padded the same way (4 zero rows)
+    assert need == 65536 + 64 * 64 * 2 + 64 * 64 * 2
     assert L.bst_workspace_bytes(3, _lib.F16, 1, 64, 64, 60, None) == 0   # no such kind
 
-    def pad(ws=None, wsb=0, **kw):
+    def pad(ws=None, wsb=0, ab=_lib.F16, c=_lib.F16, sa=None, sb=None, **kw):
         a = dict(M=64, N=64, K=60, A=ODD, lda=61, B=ODD, ldb=67, C=FAKE2, ldc=64)
         a.update(kw)
-        return L.bst_gemm_padded(_lib.F16, _lib.F16, a["M"], a["N"], a["K"], a["A"], a["lda"],
-                                 a["B"], a["ldb"], a["C"], a["ldc"], None, None, None, ws, wsb,
+        return L.bst_gemm_padded(ab, c, a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                 a["B"], a["ldb"], a["C"], a["ldc"], sa, sb, None, ws, wsb,
                                  None)
     assert pad() == _lib.E_WORKSPACE                          # odd strides are fine, ws is not
     assert pad(ws=FAKE, wsb=need - 1) == _lib.E_WORKSPACE
@@ -158,6 +159,65 @@ def test_gemm_padded_validation(L):
     assert pad(lda=59) == _lib.E_INVAL                        # lda < K
     assert pad(A=None) == _lib.E_INVAL
     assert pad(M=0) == _lib.OK
+    # Errors that only the GEMM's own checks find must still come before the
+    # operand copies are enqueued: with fake operand pointers and a fake
+    # workspace of the right size, a call that got as far as a launch would
+    # fault or report BST_E_HIP, not the documented status.
+    ws = dict(ws=FAKE, wsb=need)
+    assert pad(c=_lib.I32, **ws) == _lib.E_UNSUPPORTED        # int32 out needs int8 in
+    assert pad(C=None, **ws) == _lib.E_INVAL
+    assert pad(C=ODD, **ws) == _lib.E_ALIGN
+    assert pad(N=56, ldc=60, **ws) == _lib.E_ALIGN            # 120-byte rows of C
+    assert pad(ldc=32, **ws) == _lib.E_INVAL                  # ldc < N
+    mx_need = L.bst_workspace_bytes(2, _lib.MXE4M3, 1, 64, 64, 64, None)
+    assert pad(ab=_lib.MXE4M3, c=_lib.BF16, K=64, lda=65, ws=FAKE,
+               wsb=mx_need) == _lib.E_INVAL                   # MX scales missing
+    assert pad(ab=_lib.MXE4M3, c=_lib.BF16, K=48, lda=65, sa=FAKE, sb=FAKE, ws=FAKE,
+               wsb=1 << 20) == _lib.E_INVAL                   # MX needs K % 32 == 0
+
+
+def test_gemm_padded_runs_the_dma_family(L):
+    """The padding matmul pads K as well, so a K that is not a whole number of
+    16-byte chunks still reaches the LDS-DMA kernels when N is aligned."""
+    out = _lib.Sched()
+    for ab, K in [(_lib.F16, 250), (_lib.BF16, 1001), (_lib.I8, 250), (_lib.E4M3, 120)]:
+        assert L.bst_effective_sched(2, ab, 1, 200, 256, K, ctypes.byref(S(tile=(128, 128))),
+                                     ctypes.byref(out)) == _lib.OK
+        assert out.path == 2, (ab, K)
+        assert L.bst_effective_sched(0, ab, 1, 200, 256, K, ctypes.byref(S(tile=(128, 128))),
+                                     ctypes.byref(out)) == _lib.OK
+        assert out.path == 1, (ab, K)          # the same K unpadded: register-staged only
+    # N not aligned: the copies' extra columns would be outputs, so N is not padded
+    assert L.bst_effective_sched(2, _lib.F16, 1, 200, 250, 256, None, ctypes.byref(out)) == _lib.OK
+    assert out.path == 1
+
+
+def test_batched_c_batches_may_not_overlap(L):
+    def call(strideC):
+        return L.bst_batched_gemm(_lib.F16, _lib.F16, 3, 64, 64, 64, FAKE, 64, 0, FAKE, 64,
+                                  64 * 64, FAKE2, 72, strideC, None, None, 0, None)
+    assert call(0) == _lib.E_INVAL
+    assert call(63 * 72 + 56) == _lib.E_INVAL              # last row of batch b meets batch b+1
+    assert b"overlap" in L.bst_last_error()
+    # with no rows there is nothing to overlap
+    assert L.bst_batched_gemm(_lib.F16, _lib.F16, 3, 0, 64, 64, FAKE, 64, 0, FAKE, 64, 0, FAKE2,
+                              72, 0, None, None, 0, None) == _lib.OK
+
+
+def test_task_count(L):
+    n = ctypes.c_int64(-1)
+    assert L.bst_task_count(0, _lib.F16, 3, 200, 136, ctypes.byref(S(tile=(64, 64))),
+                            ctypes.byref(n)) == _lib.OK
+    assert n.value == 3 * 4 * 3
+    assert L.bst_task_count(1, _lib.I8, 8, 8192, 4096, ctypes.byref(S(tile=(256, 256))),
+                            ctypes.byref(n)) == _lib.OK
+    assert n.value == (32 + 8) * 16
+    assert L.bst_task_count(0, _lib.F16, 1, 1024, 1024, None, ctypes.byref(n)) == _lib.OK
+    assert n.value == 64                                     # default tile 128 x 128
+    assert L.bst_task_count(0, _lib.F16, 1, 64, 64, ctypes.byref(S(tile=(96, 96))),
+                            ctypes.byref(n)) == _lib.E_UNSUPPORTED
+    assert L.bst_task_count(2, _lib.F16, 1, 64, 64, None, ctypes.byref(n)) == _lib.E_INVAL
+    assert L.bst_task_count(0, _lib.F16, 1, 64, 64, None, None) == _lib.E_INVAL
 
 
 def test_effective_sched_shuffle_k(L):

@@ -39,6 +39,36 @@ def test_fp16_odd_strides_and_bases(orc, M, N, K, sched):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("kind", ["f16", "i8"])
+def test_padded_k_runs_lds_dma(orc, kind):
+    """K = 250 is not a whole number of 16-byte chunks: the padding GEMM pads K
+    too (zero columns of A meet zero rows of B), so with N aligned it runs the
+    LDS-DMA kernels; results match the oracle on the caller's layout (int8
+    bit-exact)."""
+    import torch
+    M, N, K = 200, 256, 250
+    g = np.random.default_rng(31)
+    ab = bst().F16 if kind == "f16" else bst().I8
+    if kind == "f16":
+        Af, Bf = _f16(g, (M, K + 3)), _f16(g, (K, N + 1))
+    else:
+        Af = g.integers(-127, 128, (M, K + 3)).astype(np.int8)
+        Bf = g.integers(-127, 128, (K, N + 1)).astype(np.int8)
+    code = orc.F16 if kind == "f16" else orc.I8
+    res = orc.gemm(code, Af, Bf, M=M, N=N, K=K, lda=K + 3, ldb=N + 1, want_acc=kind == "i8")
+    A, B = to_gpu(Af, kind)[:, :K], to_gpu(Bf, kind)[:, :N]
+    for sched in [dict(tile=(64, 64)), dict(tile=(128, 128), split_k=2, xcd_remap=1)]:
+        s = bst().make_sched(**sched)
+        assert bst().effective_sched(2, ab, 1, M, N, K, s).path == 2
+        say("padded K", kind, sched)
+        C = bst().gemm_padded(A, B, sched=s)
+        if kind == "f16":
+            check_close(orc, C, res[0], res[1], TOL_16, str(sched))
+        else:
+            assert np.array_equal(codes(C).astype(np.int64), res[2]), sched
+    torch.cuda.synchronize()
+
+
 def test_int8_odd_stride_bit_exact(orc):
     import torch
     M, N, K = 160, 96, 300
