@@ -21,12 +21,19 @@ Recipes (one per workload of the method's measurement set):
                  1..127 rows), A int8[8192][2048], B int8[8][2048][4096]
                  = U{-127..127}, row scales f32[8192] and column scales
                  f32[8][4096] = LogNormal(0, 0.5).
+* int8_slice_k -- grouped slice-K: 8 groups cutting K = 8192, sizes
+                 16 * Multinomial(512, Dirichlet(0.5 * 1_8)) (whole 16-byte
+                 units; first draw with no empty group and one group under
+                 128), A int8[1024][8192], B int8[8192][2048] = U{-127..127},
+                 row scales f32[8][1024] and column scales f32[8][2048] =
+                 LogNormal(0, 0.5); one bf16 [1024][2048] output per group.
 """
 from __future__ import annotations
 
 import numpy as np
 
-WORKLOAD_IDS = {"tails": 1, "fp16_2k": 2, "mxfp8_4k": 3, "bf16_batch": 4, "int8_groups": 5}
+WORKLOAD_IDS = {"tails": 1, "fp16_2k": 2, "mxfp8_4k": 3, "bf16_batch": 4, "int8_groups": 5,
+                "int8_slice_k": 6}
 
 
 def rng(workload_id: int, tensor_id: int) -> np.random.Generator:
@@ -102,6 +109,18 @@ def group_sizes(G=8, total=8192, workload_id=5, small=128, max_attempts=1000):
     raise RuntimeError("no acceptable group-size draw")
 
 
+def group_k_sizes(G=8, total=8192, workload_id=6, unit=16, small=128, max_attempts=1000):
+    """Slice-K group sizes in whole `unit`s: first draw with no empty group and one
+    group under `small`."""
+    for attempt in range(max_attempts):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, 100 + attempt])))
+        p = g.dirichlet(np.full(G, 0.5))
+        k = g.multinomial(total // unit, p) * unit
+        if k.min() >= unit and (k < small).any():
+            return k.astype(np.int32)
+    raise RuntimeError("no acceptable group-size draw")
+
+
 def workload(name: str, *, small: bool = False) -> dict:
     """Host arrays of one named workload.  small=True shrinks the big ones
     (same recipe, fewer rows/cols) for quick checks."""
@@ -131,6 +150,14 @@ def workload(name: str, *, small: bool = False) -> dict:
         return dict(dtype="i8", G=G, group_m=gm, total_m=total, N=N, K=K,
                     A=int8_uniform((total, K), wid, 0), B=int8_uniform((G, K, N), wid, 1),
                     row_scale=lognormal_f32((total,), wid, 2),
+                    col_scale=lognormal_f32((G, N), wid, 3), tile=(256, 256), off=1,
+                    direction="zn")
+    if name == "int8_slice_k":
+        G, M, N, total = (4, 128, 256, 1024) if small else (8, 1024, 2048, 8192)
+        gk = group_k_sizes(G, total, wid)
+        return dict(dtype="i8", G=G, group_k=gk, total_k=total, M=M, N=N,
+                    A=int8_uniform((M, total), wid, 0), B=int8_uniform((total, N), wid, 1),
+                    row_scale=lognormal_f32((G, M), wid, 2),
                     col_scale=lognormal_f32((G, N), wid, 3), tile=(256, 256), off=1,
                     direction="zn")
     raise KeyError(name)

@@ -65,6 +65,10 @@ def lib():
             L.orc_grouped_gemm.argtypes = [i32, p, i64, i64, i64, p, i64, p, i64, i64, p, p,
                                            i64, i64, i64, ctypes.c_int, p, i64, p, p, p]
             L.orc_grouped_gemm.restype = ctypes.c_int
+            L.orc_grouped_gemm_slice_k.argtypes = [ctypes.c_int, i32, p, i64, i64, i64, p, i64,
+                                                   p, i64, p, p, i64, i64, i64, ctypes.c_int, p,
+                                                   i64, p, p, p]
+            L.orc_grouped_gemm_slice_k.restype = ctypes.c_int
             L.orc_add_addend.argtypes = [i64, p, p, p]
             L.orc_add_addend.restype = ctypes.c_int
             L.orc_compare.argtypes = [i64, p, p, p, p]
@@ -170,6 +174,36 @@ def grouped_gemm(group_m, A, B, N, K, *, row_scale=None, col_scale=None, tile=(1
                                 _ptr(den), _ptr(acc))
     if rc != 0:
         raise ValueError("orc_grouped_gemm failed (%d)" % rc)
+    return ref, den, acc
+
+
+def grouped_gemm_slice_k(ab, group_k, A, B, M, N, *, total_k=None, lda=None, ldb=None,
+                         row_scale=None, col_scale=None, tile=(128, 128), off=1,
+                         direction="zn", rows=None):
+    """Grouped slice-K oracle (orc_grouped_gemm_slice_k in oracle.c): group g multiplies
+    A[:, Q_g:Q_g+k_g] by B[Q_g:Q_g+k_g, :]; outputs stacked as rows g*M + i.  A, B: raw
+    codes (uint16 f16/bf16, int8); row_scale [G][M], col_scale [G][N] (int8 only).
+    Returns (ref, den, acc) for the selected stacked rows (acc: int64, int8 only)."""
+    gk = np.ascontiguousarray(group_k, dtype=np.int32)
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    total_k = int(gk.sum()) if total_k is None else total_k
+    lda = total_k if lda is None else lda
+    ldb = N if ldb is None else ldb
+    G = len(gk)
+    nrows = G * M if rows is None else len(rows)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    ref = np.zeros((nrows, N), np.float64)
+    den = np.zeros((nrows, N), np.float64)
+    acc = np.zeros((nrows, N), np.int64)
+    rs = None if row_scale is None else np.ascontiguousarray(row_scale, dtype=np.float32)
+    cs = None if col_scale is None else np.ascontiguousarray(col_scale, dtype=np.float32)
+    rc = lib().orc_grouped_gemm_slice_k(ab, G, _ptr(gk), total_k, M, N, _ptr(A), lda, _ptr(B),
+                                        ldb, _ptr(rs), _ptr(cs), tile[0], tile[1], off,
+                                        _dir(direction), _ptr(rows_a), nrows, _ptr(ref),
+                                        _ptr(den), _ptr(acc))
+    if rc != 0:
+        raise ValueError("orc_grouped_gemm_slice_k failed (%d)" % rc)
     return ref, den, acc
 
 

@@ -17,6 +17,8 @@
  *     pages do not define; it is the row-major baseline of the comparison;
  *   - the grouped slice-M decomposition: groups concatenated in order, each
  *     re-targeted with Update (s4.2) to its own M;
+ *   - the grouped slice-K product: K cut into consecutive groups, one output
+ *     matrix per group, the groups' tasks numbered like batches (s4.4);
  *   - C = A.B in fp64 (int64 for int8), element by element, one task at a
  *     time in map order, each output element written exactly once; and the
  *     per-token / per-channel dequant out = acc * s_row[i] * s_col[g][j].
@@ -395,6 +397,106 @@ int orc_grouped_gemm(int32_t G, const int32_t *group_m, int64_t total_m, int64_t
   for (int64_t e = 0; rc == 0 && e < nrows * N; ++e)
     if (count[e] != 1) rc = -3;
   free(count); free(pos); free(map);
+  return rc;
+}
+
+/* ------------------------------------------------ grouped slice-K ----- */
+
+/*
+ * Grouped slice-K GEMM, with optional per-token / per-channel dequant
+ * ("Block Dispatch Policies" names a grouped-matmul-slice-K example and its
+ * per-token-dequant variant under the PreloadAsync policies; reading: the K
+ * dimension is cut into G consecutive groups and each group is its own
+ * product with its own output matrix).
+ *
+ * Group g owns K indices [Q_g, Q_g + group_k[g]) with Q_g the sum of the
+ * earlier groups' sizes: columns of A (row-major [M][lda], total_k columns
+ * allocated) and rows of B (row-major [total_k][ldb]).  Its output is
+ * C_g = A[:, Q_g : Q_g + k_g] . B[Q_g : Q_g + k_g, :], an M x N matrix; the
+ * outputs are stacked as rows g*M + i.  An empty group (k_g = 0) has an
+ * all-zero output.  Every group shares M and N, so the tasks are those of
+ * a batched problem with G batches: task t belongs to group t / core and
+ * maps its local index with the block map (s4.3, s4.4, s4.5, s4.6).
+ *
+ * acc (int8 only) receives the exact int64 sums.  ref / den as in orc_gemm:
+ * ref = the exact sum (fp64; int8: the int64 sum), den = the sum of
+ * |products|; with row_scale ([G][M]: per group and token row) and
+ * col_scale ([G][N]: per group and channel), int8 only, ref = acc *
+ * row_scale[g*M + i] * col_scale[g*N + j] and den is scaled by
+ * |row_scale * col_scale|.  Rows select stacked rows g*M + i as in orc_gemm.
+ * Returns 0, -1 on bad arguments (negative group size, sizes summing past
+ * total_k, scales with non-int8 operands), -3 if an element was written
+ * other than once.
+ */
+int orc_grouped_gemm_slice_k(int ab, int32_t G, const int32_t *group_k, int64_t total_k,
+                             int64_t M, int64_t N, const void *A, int64_t lda,
+                             const void *B, int64_t ldb,
+                             const float *row_scale, const float *col_scale,
+                             int64_t tm, int64_t tn, int64_t off, int dir,
+                             const int64_t *rows, int64_t nrows,
+                             double *ref, double *den, int64_t *acc) {
+  if (G < 0 || M < 0 || N < 0 || total_k < 0 || tm <= 0 || tn <= 0 || off <= 0) return -1;
+  if (ab != ORC_F16 && ab != ORC_BF16 && ab != ORC_I8) return -1;
+  if ((row_scale || col_scale) && (ab != ORC_I8 || !row_scale || !col_scale)) return -1;
+  int64_t *q = (int64_t *)malloc(sizeof(int64_t) * (size_t)(G + 1));
+  if (!q) return -1;
+  q[0] = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    if (group_k[g] < 0) { free(q); return -1; }
+    q[g + 1] = q[g] + group_k[g];
+  }
+  if (q[G] > total_k) { free(q); return -1; }
+  int64_t loopsM = cdiv(M, tm), loopsN = cdiv(N, tn), core = loopsM * loopsN;
+  int64_t T = (int64_t)G * core;
+  int64_t total_rows = (int64_t)G * M;
+  if (!rows) nrows = total_rows;
+  int64_t *pos = row_positions(total_rows, rows, nrows);
+  if (!pos) { free(q); return -1; }
+  uint8_t *count = (uint8_t *)calloc((size_t)(nrows * N > 0 ? nrows * N : 1), 1);
+  if (!count) { free(q); free(pos); return -1; }
+  int bad = 0;
+
+  #pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t g = t / core, inner = t % core, m, n;       /* the group, like s4.4 */
+    if (block_coord(loopsM, loopsN, off, dir, inner, &m, &n)) { bad |= 1; continue; }
+    int64_t mAct = (m == loopsM - 1) ? (M - m * tm) : tm;
+    int64_t nAct = (n == loopsN - 1) ? (N - n * tn) : tn;
+    for (int64_t i = m * tm; i < m * tm + mAct; ++i) {
+      int64_t p = pos[g * M + i];
+      if (p < 0) continue;
+      for (int64_t j = n * tn; j < n * tn + nAct; ++j) {
+        double s = 0.0, d = 0.0;
+        int64_t si = 0, di = 0;
+        for (int64_t k = q[g]; k < q[g + 1]; ++k) {
+          if (ab == ORC_I8) {
+            int64_t x = (int64_t)((const int8_t *)A)[i * lda + k] *
+                        (int64_t)((const int8_t *)B)[k * ldb + j];
+            si += x; di += x < 0 ? -x : x;
+          } else {
+            double x = elem(ab, A, i * lda + k) * elem(ab, B, k * ldb + j);
+            s += x; d += fabs(x);
+          }
+        }
+        if (ab == ORC_I8) { s = (double)si; d = (double)di; }
+        if (row_scale) {
+          double rs = (double)row_scale[g * M + i], cs = (double)col_scale[g * N + j];
+          ref[p * N + j] = s * rs * cs;
+          den[p * N + j] = d * fabs(rs * cs);
+        } else {
+          ref[p * N + j] = s;
+          den[p * N + j] = d;
+        }
+        if (acc) acc[p * N + j] = si;
+        #pragma omp atomic
+        count[p * N + j] += 1;
+      }
+    }
+  }
+  int rc = bad ? -1 : 0;
+  for (int64_t e = 0; rc == 0 && e < nrows * N; ++e)
+    if (count[e] != 1) rc = -3;
+  free(count); free(pos); free(q);
   return rc;
 }
 
