@@ -8,7 +8,7 @@ and raises :class:`BstError` on a non-OK status.  All computation runs in the
 HIP kernels of libbst.so; there is no CPU path.
 
 Names follow the C ABI without the ``bst_`` prefix: :func:`gemm`,
-:func:`batched_gemm`, :func:`grouped_gemm_slice_m`,
+:func:`batched_gemm`, :func:`grouped_gemm_slice_m`, :func:`grouped_gemm_slice_k`,
 :func:`quant_gemm_per_token`, :func:`tile_map`, :func:`grouped_tile_map`,
 :func:`workspace_bytes`, :func:`effective_sched`.
 """
@@ -22,7 +22,8 @@ from ._lib import (BF16, E4M3, F16, F32, I8, I32, MXE4M3, BstError, Sched, check
 ZN, NZ, RASTER = 0, 1, 2
 _DIRS = {"zn": ZN, "nz": NZ, "raster": RASTER}
 
-__all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_gemm", "grouped_gemm_slice_m",
+__all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_gemm",
+           "grouped_gemm_slice_m", "grouped_gemm_slice_k",
            "quant_gemm_per_token", "tile_map", "grouped_tile_map", "workspace_bytes",
            "effective_sched", "task_count", "version", "LIB_PATH"]
 
@@ -132,7 +133,8 @@ def _sched(s):
 
 
 def workspace_bytes(kind, ab, count, M, N, K, sched=None):
-    """Workspace bytes (kind 0: plain/batched with count = batch, 1: grouped with count = G)."""
+    """Workspace bytes (kind 0: plain/batched with count = batch, 1: grouped slice-M with
+    count = G, 2: padding GEMM, 3: grouped slice-K with count = G and K = total_k)."""
     return lib().bst_workspace_bytes(kind, ab, count, M, N, K, _sched(sched))
 
 
@@ -219,6 +221,35 @@ def grouped_gemm_slice_m(A, B, group_m, C=None, *, row_scale=None, col_scale=Non
                                          _ptr(B), _ld(B), B.stride(0), _ptr(C), _ld(C),
                                          _ptr(row_scale), _ptr(col_scale), _sched(sched),
                                          _ptr(ws), wsb, _stream(A.device)))
+    return C
+
+
+def grouped_gemm_slice_k(A, B, group_k, C=None, *, row_scale=None, col_scale=None,
+                         out_dtype=None, sched=None, workspace=None):
+    """K cut into groups: group g multiplies A[:, Q_g:Q_g+k_g] by B[Q_g:Q_g+k_g, :] into
+    C[g] (A [M][total_k], B [total_k][N], C [G][M][N]); group_k is a device int32 tensor of
+    G sizes (never read on the host); row_scale [G][M] / col_scale [G][N] for int8 dequant."""
+    torch = _torch()
+    _dev(A, B, C, group_k, row_scale, col_scale)
+    if group_k.dtype != torch.int32:
+        raise TypeError("group_k must be int32")
+    ab = _code(A.dtype)
+    M, total_k = A.shape
+    N = B.shape[1]
+    G = group_k.numel()
+    if C is None:
+        if out_dtype is None:
+            out_dtype = torch.bfloat16 if row_scale is not None else (
+                torch.int32 if ab == I8 else A.dtype)
+        C = torch.empty((G, M, N), dtype=out_dtype, device=A.device)
+    c = _code(C.dtype)
+    nb = workspace_bytes(3, ab, G, M, N, total_k, sched)
+    ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(nb, A.device)
+    check(lib().bst_grouped_gemm_slice_k(ab, c, G, _ptr(group_k), total_k, M, N, _ptr(A), _ld(A),
+                                         _ptr(B), _ld(B), _ptr(C), _ld(C),
+                                         C.stride(0) if C.dim() == 3 else 0, _ptr(row_scale),
+                                         _ptr(col_scale), _sched(sched), _ptr(ws), wsb,
+                                         _stream(A.device)))
     return C
 
 

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "BST_OK", -1: "BST_E_INVAL", -2: "BST_E_UNSUPPORTED", -3: "BS
 # bst_dtype
 F16, BF16, E4M3, MXE4M3, I8, I32, F32 = 1, 2, 3, 4, 5, 6, 7
 
-EXPORTS = ["bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm", "bst_grouped_gemm_slice_m", "bst_quant_gemm_per_token",
+EXPORTS = ["bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
+           "bst_grouped_gemm_slice_m", "bst_grouped_gemm_slice_k", "bst_quant_gemm_per_token",
            "bst_tile_map", "bst_grouped_tile_map", "bst_workspace_bytes", "bst_effective_sched",
            "bst_task_count", "bst_last_error", "bst_version"]
 
@@ -54,6 +55,8 @@ def lib():
                                            i64, i64, sp, p, sz, p]
             L.bst_grouped_gemm_slice_m.argtypes = [st, st, i32, p, i64, i64, i64, p, i64, p, i64,
                                                    i64, p, i64, p, p, sp, p, sz, p]
+            L.bst_grouped_gemm_slice_k.argtypes = [st, st, i32, p, i64, i64, i64, p, i64, p, i64,
+                                                   p, i64, i64, p, p, sp, p, sz, p]
             L.bst_quant_gemm_per_token.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, st,
                                                    sp, p, sz, p]
             L.bst_tile_map.argtypes = [st, i64, i64, i64, sp, p, i64, p]
@@ -63,7 +66,8 @@ def lib():
             L.bst_effective_sched.argtypes = [ctypes.c_int, st, i64, i64, i64, i64, sp, sp]
             L.bst_task_count.argtypes = [ctypes.c_int, st, i64, i64, i64, sp,
                                          ctypes.POINTER(i64)]
-            for fn in ("bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm", "bst_grouped_gemm_slice_m",
+            for fn in ("bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
+                       "bst_grouped_gemm_slice_m", "bst_grouped_gemm_slice_k",
                        "bst_quant_gemm_per_token", "bst_tile_map", "bst_grouped_tile_map",
                        "bst_effective_sched", "bst_task_count"):
                 getattr(L, fn).restype = st

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["bst.hip", "inst_f16.hip", "inst_bf16.hip", "inst_i8.hip", "inst_fp8.hip",
-           "inst_mxfp8.hip"]
+           "inst_mxfp8.hip", "inst_slicek.hip"]
 HEADERS = ["bst_device.hpp", "bst_kernel_dma.hpp", "bst_instances.hpp"]
 DEPS = ([os.path.join(CSRC, f) for f in SOURCES + HEADERS] +
         [os.path.join(ROOT, "include", "bst.h")])

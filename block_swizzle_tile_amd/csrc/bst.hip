@@ -34,15 +34,15 @@ bst_status fail(bst_status st, const char* fmt, ...) {
 
 int kernel_ab(bst_dtype ab) { return (int)ab; }
 
-const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, bool grouped, bool dma,
+const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, int form, bool dma,
                               bool add = false) {
   const InstanceList lists[] = {instances_f16(), instances_bf16(), instances_i8(),
-                                instances_fp8(), instances_mxfp8()};
+                                instances_fp8(), instances_mxfp8(), instances_slicek()};
   for (const InstanceList& l : lists)
     for (int i = 0; i < l.count; ++i) {
       const Instance& in = l.begin[i];
       if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
-          in.grouped == grouped && in.dma == dma && in.add == add)
+          in.form == form && in.dma == dma && in.add == add)
         return &in;
     }
   return nullptr;
@@ -131,9 +131,10 @@ struct Plan {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Resolves the schedule.  kind 0: plain / batched (count = batch), kind 1:
-// grouped (count = G, M = total_m).  Validates the schedule fields and the
-// sizes that bound the task count; pointer checks are the callers'.
+// Resolves the schedule.  form FORM_DENSE: plain / batched (count = batch),
+// FORM_SLICE_M: grouped slice-M (count = G, M = total_m), FORM_SLICE_K:
+// grouped slice-K (count = G, K = total_k).  Validates the schedule fields
+// and the sizes that bound the task count; pointer checks are the callers'.
 // Layout facts that decide whether the LDS-DMA family can run a call.
 struct Layout {
   int64_t lda = 0, ldb = 0;
@@ -154,16 +155,17 @@ bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, cons
   return true;
 }
 
-bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
+bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
                      const bst_sched* s, bool need_device, Plan& p, const Layout* L = nullptr,
                      bool add = false) {
+  const bool grouped = form != FORM_DENSE;
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (count < 0 || M < 0 || N < 0 || K < 0)
     return fail(BST_E_INVAL, "negative size (count %lld M %lld N %lld K %lld)", (long long)count,
                 (long long)M, (long long)N, (long long)K);
   if (M > kMaxU32 || N > kMaxU32 || K > kMaxU32 || count > kMaxU32)
     return fail(BST_E_INVAL, "size above 2^31-1");
-  if (kind == 1 && (count < 1 || count > kMaxGroups))
+  if (grouped && (count < 1 || count > kMaxGroups))
     return fail(BST_E_INVAL, "group count %lld outside [1, %d]", (long long)count, kMaxGroups);
   if (ab == BST_MXE4M3 && K % 32 != 0)
     return fail(BST_E_INVAL, "MX operands need K %% 32 == 0 (K = %lld)", (long long)K);
@@ -186,14 +188,19 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
   if (d.shuffle_k > 1) return fail(BST_E_INVAL, "shuffle_k must be 0 or 1");
   // matmul-add runs only the LDS-DMA instances built with the addend epilogue
-  const Instance* reg = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, kind == 1, false);
-  const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, kind == 1, true, add);
+  const Instance* reg = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, form, false);
+  const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, form, true, add);
   if (!reg && !dma)
     return fail(BST_E_UNSUPPORTED, "no %s kernel for dtype %d with tile %ux%u",
-                add ? "matmul-add" : kind == 1 ? "grouped" : "plain", (int)ab, d.tile_m,
+                add ? "matmul-add" : form == FORM_SLICE_M ? "grouped slice-M"
+                : form == FORM_SLICE_K ? "grouped slice-K" : "plain", (int)ab, d.tile_m,
                 d.tile_n);
   const Layout lay = L ? *L : Layout{K, N, nullptr, nullptr};
-  const bool fits = dma && dma_fits(ab, N, K, d.tile_m, (uint32_t)dma->bk, lay);
+  // slice-K: the kernels check each group's chunk alignment on the device,
+  // so the total K need not be whole chunks
+  const int64_t ce = 16 / (int64_t)elem_size(ab);
+  const int64_t kfit = form == FORM_SLICE_K ? (K + ce - 1) / ce * ce : K;
+  const bool fits = dma && dma_fits(ab, N, kfit, d.tile_m, (uint32_t)dma->bk, lay);
   if (d.path == 2 && !fits)
     return fail(BST_E_UNSUPPORTED, "the LDS-DMA kernels need K and N in whole 16-byte chunks "
                 "(and K %% 128 == 0 for MX); use path 0 or 1");
@@ -210,11 +217,13 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   p.remap = d.xcd_remap;
   p.shuffle = p.inst->dma ? d.shuffle_k : 0u;  // the register-staged family runs stages in order
   const int64_t loopsN = cdiv64(N, p.bn);
-  const int64_t tiles = kind == 1 ? (cdiv64(M, p.bm) + count) * loopsN
-                                  : count * cdiv64(M, p.bm) * loopsN;
+  const int64_t tiles = form == FORM_SLICE_M ? (cdiv64(M, p.bm) + count) * loopsN
+                                             : count * cdiv64(M, p.bm) * loopsN;
   if (tiles > kMaxU32) return fail(BST_E_INVAL, "task count %lld above 2^31-1", (long long)tiles);
   p.tile_cap = (uint64_t)tiles;
-  const int64_t nk = cdiv64(K, p.bk);
+  // slice-K groups split their own K on the device (whole stages per slice,
+  // empty slices allowed); the automatic split judges by the mean group
+  const int64_t nk = cdiv64(form == FORM_SLICE_K ? cdiv64(K, count) : K, p.bk);
   int64_t split = d.split_k;
   const int cus = need_device ? device_cus() : 256;
   if (split == 0) {
@@ -225,7 +234,9 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   }
   if (nk == 0) split = 1;
   int64_t kslice_steps = nk > 0 ? cdiv64(nk, split) : 0;
-  if (kslice_steps > 0) split = cdiv64(nk, kslice_steps);  // no empty slices
+  // no empty slices (slice-K groups differ in size: the requested split
+  // stands, and a short group's surplus slices are empty)
+  if (kslice_steps > 0 && form != FORM_SLICE_K) split = cdiv64(nk, kslice_steps);
   p.split = (uint32_t)split;
   p.kslice = (uint32_t)(kslice_steps * p.bk);
   if (tiles * split > kMaxU32) return fail(BST_E_INVAL, "work-unit count above 2^31-1");
@@ -242,6 +253,12 @@ bst_status make_plan(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, units > 0 ? units : 1));
   p.grid = (uint32_t)grid;
   return BST_OK;
+}
+
+// Problem form of a public `kind` code: 0 plain / batched, 1 grouped
+// slice-M, 2 the GEMM of the padding matmul (a plain one), 3 grouped slice-K.
+int kind_form(int kind) {
+  return kind == 1 ? FORM_SLICE_M : kind == 3 ? FORM_SLICE_K : FORM_DENSE;
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -290,7 +307,7 @@ bst_status prepare_dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, in
   empty = true;
   if (!is_ab(ab)) return fail(BST_E_INVAL, "unknown operand dtype %d", (int)ab);
   if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
-  bst_status st = make_plan(0, ab, batch, M, N, K, s, false, p, nullptr, X != nullptr);
+  bst_status st = make_plan(FORM_DENSE, ab, batch, M, N, K, s, false, p, nullptr, X != nullptr);
   if (st != BST_OK) return st;
   if (batch == 0 || M == 0 || N == 0) return BST_OK;
   const size_t es = elem_size(ab), ec = elem_size(c);
@@ -320,7 +337,7 @@ bst_status prepare_dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, in
                  (batch > 1 && (!stride_ok(strideA, es) || !stride_ok(strideB, es))))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
   const Layout lay{lda, ldb, sa, sb};
-  st = make_plan(0, ab, batch, M, N, K, s, true, p, &lay, X != nullptr);
+  st = make_plan(FORM_DENSE, ab, batch, M, N, K, s, true, p, &lay, X != nullptr);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
@@ -495,11 +512,11 @@ bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int6
   // the caller's K decides what is valid (MX blocks, the int8 bound); the
   // GEMM then runs at the padded depth
   Plan p;
-  bst_status st = make_plan(0, ab, 1, M, N, K, s, false, p);
+  bst_status st = make_plan(FORM_DENSE, ab, 1, M, N, K, s, false, p);
   if (st != BST_OK) return st;
   const Padded q = padded_layout(ab, M, N, K);
   const Layout lay{q.lda, q.ldb, scale_a, scale_b};
-  st = make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay);
+  st = make_plan(FORM_DENSE, ab, 1, M, N, q.kp, s, true, p, &lay);
   if (st != BST_OK) return st;
   // The GEMM's own workspace comes first, its split-K counters at offset 0
   // whatever the split, so that a workspace shared with other calls keeps
@@ -562,7 +579,7 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
   if (row_scale && (ab != BST_I8 || c == BST_I32))
     return fail(BST_E_INVAL, "dequant scales need int8 operands and a floating output");
   Plan p;
-  bst_status st = make_plan(1, ab, G, total_m, N, K, s, false, p);
+  bst_status st = make_plan(FORM_SLICE_M, ab, G, total_m, N, K, s, false, p);
   if (st != BST_OK) return st;
   if (!group_m) return fail(BST_E_INVAL, "group_m is NULL");
   if (total_m == 0 || N == 0) return BST_OK;
@@ -576,7 +593,7 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
                  !stride_ok(strideB, es))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
   const Layout lay{lda, ldb, nullptr, nullptr};
-  st = make_plan(1, ab, G, total_m, N, K, s, true, p, &lay);
+  st = make_plan(FORM_SLICE_M, ab, G, total_m, N, K, s, true, p, &lay);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
   if (st != BST_OK) return st;
@@ -601,13 +618,72 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
   return launch(p, a, stream);
 }
 
+bst_status bst_grouped_gemm_slice_k(bst_dtype ab, bst_dtype c, int32_t G, const int32_t* group_k,
+                                    int64_t total_k, int64_t M, int64_t N, const void* A,
+                                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                    int64_t strideC, const float* row_scale,
+                                    const float* col_scale, const bst_sched* s, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (ab != BST_I8 && ab != BST_F16 && ab != BST_BF16)
+    return fail(BST_E_UNSUPPORTED, "grouped slice-K GEMM takes int8, f16 or bf16 operands");
+  if (!out_ok(ab, c)) return fail(BST_E_UNSUPPORTED, "output dtype %d with operands %d", (int)c, (int)ab);
+  if ((row_scale == nullptr) != (col_scale == nullptr))
+    return fail(BST_E_INVAL, "give both dequant scales or neither");
+  if (row_scale && (ab != BST_I8 || c == BST_I32))
+    return fail(BST_E_INVAL, "dequant scales need int8 operands and a floating output");
+  Plan p;
+  bst_status st = make_plan(FORM_SLICE_K, ab, G, M, N, total_k, s, false, p);
+  if (st != BST_OK) return st;
+  if (!group_k) return fail(BST_E_INVAL, "group_k is NULL");
+  if (M == 0 || N == 0) return BST_OK;
+  const size_t es = elem_size(ab), ec = elem_size(c);
+  const bool has_k = total_k > 0;  // with no K at all, A and B are never read
+  if (!C || (has_k && (!A || !B))) return fail(BST_E_INVAL, "A, B or C is NULL");
+  if ((has_k && (lda < total_k || ldb < N)) || ldc < N)
+    return fail(BST_E_INVAL, "leading dimension too small (lda %lld total_k %lld, ldb %lld, "
+                "ldc %lld, N %lld)", (long long)lda, (long long)total_k, (long long)ldb,
+                (long long)ldc, (long long)N);
+  if (G > 1 && (strideC < 0 || strideC < (M - 1) * ldc + N))
+    return fail(BST_E_INVAL, "strideC %lld lets the groups' outputs overlap (need >= %lld)",
+                (long long)strideC, (long long)((M - 1) * ldc + N));
+  if (!aligned16(C) || !stride_ok(ldc, ec) || (G > 1 && !stride_ok(strideC, ec)) ||
+      (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es))))
+    return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
+  const Layout lay{lda, ldb, nullptr, nullptr};
+  st = make_plan(FORM_SLICE_K, ab, G, M, N, total_k, s, true, p, &lay);
+  if (st != BST_OK) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != BST_OK) return st;
+  GemmArgs a{};
+#ifdef BST_TRACE
+  a.trace = g_trace;
+#endif
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint8_t*>(C);
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+  a.strideC = G > 1 ? strideC : 0;
+  a.row_scale = row_scale;
+  a.col_scale = col_scale;
+  a.group_k = group_k;
+  a.G = G;
+  a.total_k = total_k;
+  a.M = (uint32_t)M; a.N = (uint32_t)N; a.K = (uint32_t)total_k;
+  a.batch = (uint32_t)G;
+  a.tiles = (uint32_t)p.tile_cap;
+  a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
+  a.cdtype = (uint32_t)c;
+  fill_ws(a, p, ws);
+  return launch(p, a, stream);
+}
+
 bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const bst_sched* s,
                         uint32_t* out, int64_t max_tasks, void* stream) {
   Plan p;
   bst_sched d{};
   if (s) d = *s;
   d.split_k = 1;
-  bst_status st = make_plan(0, ab, batch, M, N, 0, s ? &d : nullptr, false, p);
+  bst_status st = make_plan(FORM_DENSE, ab, batch, M, N, 0, s ? &d : nullptr, false, p);
   if (st != BST_OK) return st;
   if (p.tile_cap == 0) return BST_OK;
   if (!out) return fail(BST_E_INVAL, "out is NULL");
@@ -640,7 +716,7 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
   bst_sched d{};
   if (s) d = *s;
   d.split_k = 1;
-  bst_status st = make_plan(1, ab, G, total_m, N, 0, s ? &d : nullptr, false, p);
+  bst_status st = make_plan(FORM_SLICE_M, ab, G, total_m, N, 0, s ? &d : nullptr, false, p);
   if (st != BST_OK) return st;
   if (!group_m || !out) return fail(BST_E_INVAL, "group_m or out is NULL");
   if ((int64_t)p.tile_cap > max_tasks)
@@ -670,33 +746,33 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m,
 size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N, int64_t K,
                            const bst_sched* s) {
   Plan p;
-  if (kind < 0 || kind > 2) {
-    fail(BST_E_INVAL, "kind must be 0, 1 or 2");
+  if (kind < 0 || kind > 3) {
+    fail(BST_E_INVAL, "kind must be 0, 1, 2 or 3");
     return 0;
   }
   if (kind == 2) {  // bst_gemm_padded: the split-K workspace, then the repacked operands
     if (!is_ab(ab) || M < 0 || N < 0 || K < 0) return 0;
-    if (make_plan(0, ab, 1, M, N, K, s, false, p) != BST_OK) return 0;
+    if (make_plan(FORM_DENSE, ab, 1, M, N, K, s, false, p) != BST_OK) return 0;
     const Padded q = padded_layout(ab, M, N, K);
     const Layout lay{q.lda, q.ldb, nullptr, nullptr};
-    if (make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay) != BST_OK) return 0;
+    if (make_plan(FORM_DENSE, ab, 1, M, N, q.kp, s, true, p, &lay) != BST_OK) return 0;
     return padded_gemm_ws(p) + q.bytes;
   }
-  if (make_plan(kind, ab, count, M, N, K, s, true, p) != BST_OK) return 0;
+  if (make_plan(kind_form(kind), ab, count, M, N, K, s, true, p) != BST_OK) return 0;
   return p.ws_bytes;
 }
 
 bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                                int64_t K, const bst_sched* s, bst_sched* out) {
   if (!out) return fail(BST_E_INVAL, "out is NULL");
-  if (kind < 0 || kind > 2) return fail(BST_E_INVAL, "kind must be 0, 1 or 2");
+  if (kind < 0 || kind > 3) return fail(BST_E_INVAL, "kind must be 0, 1, 2 or 3");
   Plan p;
-  bst_status st = make_plan(kind == 2 ? 0 : kind, ab, count, M, N, K, s, true, p);
+  bst_status st = make_plan(kind_form(kind), ab, count, M, N, K, s, true, p);
   if (st != BST_OK) return st;
   if (kind == 2) {  // the GEMM bst_gemm_padded runs on the repacked operands
     const Padded q = padded_layout(ab, M, N, K);
     const Layout lay{q.lda, q.ldb, nullptr, nullptr};
-    st = make_plan(0, ab, 1, M, N, q.kp, s, true, p, &lay);
+    st = make_plan(FORM_DENSE, ab, 1, M, N, q.kp, s, true, p, &lay);
     if (st != BST_OK) return st;
   }
   out->tile_m = p.bm;
@@ -715,12 +791,12 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
 bst_status bst_task_count(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                           const bst_sched* s, int64_t* tasks) {
   if (!tasks) return fail(BST_E_INVAL, "tasks is NULL");
-  if (kind != 0 && kind != 1) return fail(BST_E_INVAL, "kind must be 0 or 1");
+  if (kind != 0 && kind != 1 && kind != 3) return fail(BST_E_INVAL, "kind must be 0, 1 or 3");
   bst_sched d{};
   if (s) d = *s;
   d.split_k = 1;
   Plan p;
-  const bst_status st = make_plan(kind, ab, count, M, N, 0, s ? &d : nullptr, false, p);
+  const bst_status st = make_plan(kind_form(kind), ab, count, M, N, 0, s ? &d : nullptr, false, p);
   if (st != BST_OK) return st;
   *tasks = (int64_t)p.tile_cap;
   return BST_OK;

@@ -29,6 +29,12 @@
 namespace bst {
 
 enum AbKind { AB_F16 = 1, AB_BF16 = 2, AB_E4M3 = 3, AB_MXE4M3 = 4, AB_I8 = 5 };
+// Problem forms a kernel instance is built for: plain or batched (the batch
+// index of task t is t / tiles per batch), grouped slice-M (groups stacked
+// along M, group table of first tasks and rows), grouped slice-K (K cut
+// into groups, one output per group; tasks numbered like batches, group
+// table of first K indices).
+enum Form { FORM_DENSE = 0, FORM_SLICE_M = 1, FORM_SLICE_K = 2 };
 enum OutKind { OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 6, OUT_F32 = 7 };
 
 constexpr int kRowBytes = 128;      // bytes of one LDS row = one K stage of one row
@@ -61,9 +67,11 @@ struct GemmArgs {
   int64_t ldsa, ldsb;
   const float* row_scale;             // dequant, per stacked row
   const float* col_scale;             // dequant, [G][N]
-  const int32_t* group_m;             // grouped: device int32[G]
+  const int32_t* group_m;             // grouped slice-M: device int32[G] row counts
+  const int32_t* group_k;             // grouped slice-K: device int32[G] K counts
   int32_t G;
-  int64_t total_m;                    // grouped: rows allocated in A and C
+  int64_t total_m;                    // grouped slice-M: rows allocated in A and C
+  int64_t total_k;                    // grouped slice-K: K columns / rows allocated in A / B
   uint32_t M, N, K;                   // M unused when grouped
   uint32_t batch;
   uint32_t tiles;                     // non-grouped: batch * loopsM * loopsN
@@ -129,6 +137,7 @@ struct Task {
   uint32_t mAct, nAct;
   int64_t row0;      // first row of the tile in the (stacked) A / C
   uint32_t rows_valid;  // rows of the tile inside the allocation (<= mAct)
+  uint32_t poison = 0;  // slice-K group the LDS-DMA kernels cannot take: NaN / INT32_MIN out
 };
 
 // Grouped problems: per-workgroup table in LDS of each group's first task
@@ -160,6 +169,47 @@ __device__ __forceinline__ void build_group_table(GroupTable& gt, const GemmArgs
                                                   uint32_t loopsN) {
   if (threadIdx.x == 0) fill_group_table(gt, a.group_m, a.G, a.total_m, BM, loopsN);
   __syncthreads();
+}
+
+// Grouped slice-K: first_row[g] holds the group's first K index (the
+// earlier groups' sizes summed), first_row[G] the end of the last group.
+// Sizes below 0 count as 0 and a group is cut to the K still left of
+// total_k, so no group reads past the allocation.
+__host__ __device__ inline void fill_k_table(GroupTable& gt, const int32_t* group_k, int G,
+                                             int64_t total_k) {
+  int64_t q = 0;
+  for (int g = 0; g < G; ++g) {
+    gt.first_row[g] = q;
+    int64_t kg = group_k[g] > 0 ? group_k[g] : 0;
+    if (kg > total_k - q) kg = total_k - q;
+    q += kg;
+  }
+  gt.first_row[G] = q;
+}
+
+__device__ __forceinline__ void build_k_table(GroupTable& gt, const GemmArgs& a) {
+  if (threadIdx.x == 0) fill_k_table(gt, a.group_k, a.G, a.total_k);
+  __syncthreads();
+}
+
+// K range [k0, k1) of slice s of a task whose K runs over [kq, kq + kg):
+// slices of ks elements (a multiple of the stage depth), the last one
+// shorter, slices past the end empty (k0 >= k1).
+struct KRange {
+  uint32_t k0, k1;
+};
+__host__ __device__ __forceinline__ KRange slice_range(uint32_t kq, uint32_t kg, uint32_t ks,
+                                                       uint32_t s) {
+  const uint32_t lo = s * ks;
+  const uint32_t hi = (lo >= kg || kg - lo < ks) ? kg : lo + ks;
+  return KRange{kq + lo, kq + hi};
+}
+
+// Slice length of a slice-K group of kg elements cut into `split` slices of
+// whole stages of depth bk.
+__host__ __device__ __forceinline__ uint32_t group_kslice(uint32_t kg, uint32_t split, uint32_t bk) {
+  const uint32_t stages = (kg + bk - 1) / bk;
+  return (stages + split - 1) / split * bk;
 }
 
 __host__ __device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t t, uint32_t BM, uint32_t BN,
@@ -294,8 +344,12 @@ __device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t chunk) {
 }
 
 // 16 bytes from global memory, `valid` of them kept (the rest read as 0).
+// A 16-byte-aligned whole chunk is one vector load; anything else (a tail,
+// or a chunk that starts mid-way, as slice-K groups of any size make) is
+// read byte by byte.
 __device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
-  if (valid >= 16) return *reinterpret_cast<const u32x4_t*>(p);
+  if (valid >= 16 && ((uintptr_t)p & 15u) == 0) return *reinterpret_cast<const u32x4_t*>(p);
+  if (valid > 16) valid = 16;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (valid > 0) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -310,7 +364,7 @@ __device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
 // ------------------------------------------------------------ epilogue --
 // Shared by both kernel families: the fixed-order split-K fix-up and the
 // conversion / dequant / masked store of a wave's 32x32 sub-tiles.
-template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+template <int AB, int BM, int BN, int WM, int WN, int FORM>
 struct Epilogue {
   using T = Traits<AB>;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -491,8 +545,13 @@ struct Epilogue {
     wm = fresh_s(__builtin_amdgcn_readfirstlane(wm));  // wave-uniform in both families
     wn = fresh_s(__builtin_amdgcn_readfirstlane(wn));
     const uint32_t l32 = lane & 31u, hi = lane >> 5;
-    uint8_t* cbase = a.C + ((int64_t)(GROUPED ? 0 : tk.idx) * a.strideC + tk.row0 * a.ldc +
-                            (int64_t)tk.n * BN) * OS;
+    // slice-M tasks address C by their stacked row; batches and slice-K
+    // groups own a C each, strideC apart
+    uint8_t* cbase = a.C + ((int64_t)(FORM == FORM_SLICE_M ? 0 : tk.idx) * a.strideC +
+                            tk.row0 * a.ldc + (int64_t)tk.n * BN) * OS;
+    // dequant row scales: per stacked row (slice-M), per group and row
+    // (slice-K), per row (plain)
+    const int64_t rs0 = (FORM == FORM_SLICE_K ? (int64_t)tk.idx * a.M : 0) + tk.row0;
     // matmul-add (plain GEMM only, so the task's row0 is its first row of X)
     const uint8_t* xbase = ADD ? a.X + (tk.row0 * a.ldx + (int64_t)tk.n * BN) * OS : nullptr;
     // Dequant scales are gathered before the first store when they fit in a
@@ -504,12 +563,12 @@ struct Epilogue {
     float csv[FN][4][4];
     const float* csb = nullptr;
     if constexpr (DEQ)
-      csb = a.col_scale + (int64_t)(GROUPED ? tk.idx : 0) * a.N + (int64_t)tk.n * BN;
+      csb = a.col_scale + (int64_t)(FORM == FORM_DENSE ? 0 : tk.idx) * a.N + (int64_t)tk.n * BN;
     if constexpr (PRE) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t ml = wm * TM + i * 32 + l32;
-        rsv[i] = (FULL || ml < tk.rows_valid) ? a.row_scale[tk.row0 + ml] : 0.0f;
+        rsv[i] = (FULL || ml < tk.rows_valid) ? a.row_scale[rs0 + ml] : 0.0f;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -535,7 +594,7 @@ struct Epilogue {
         if constexpr (PRE)
           rs = rsv[i];
         else if constexpr (DEQ)
-          rs = a.row_scale[tk.row0 + ml];
+          rs = a.row_scale[rs0 + ml];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -567,6 +626,15 @@ struct Epilogue {
               }
             }
             if constexpr (ADD) add_x<OUT>(f, iv, xrow + nl * OS, whole, tk.nAct - nl);
+            if constexpr (FORM == FORM_SLICE_K) {
+              if (tk.poison) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  f[r] = __builtin_nanf("");
+                  iv[r] = (int32_t)0x80000000u;
+                }
+              }
+            }
             uint8_t* p = crow + nl * OS;
             if constexpr (STAGED) {
               lds_byte_t* q = stage + (ml - pass * RP) * PITCH + nl * OS;
@@ -716,7 +784,7 @@ struct Epilogue {
 
 };
 
-template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+template <int AB, int BM, int BN, int WM, int WN, int FORM>
 struct GemmKernel {
   using T = Traits<AB>;
   static constexpr int NT = 64 * WM * WN;
@@ -736,7 +804,8 @@ struct GemmKernel {
   static constexpr int LDS_BYTES = 2 * (STAGE_BYTES + SCALE_BYTES);
   using Acc = typename std::conditional<T::IS_INT, i32x16_t, f32x16_t>::type;
   using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
-  using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
+  using Epi = Epilogue<AB, BM, BN, WM, WN, FORM>;
+  static constexpr bool GROUPED = FORM == FORM_SLICE_M;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(T::BK * T::ES == kRowBytes, "one stage = one 128-byte row");
@@ -750,15 +819,18 @@ struct GemmKernel {
     uint32_t sa, sb;  // MX: 4 scale bytes (one per 32-wide K block) of one A row / B column
   };
 
+  // a_al: A's 16-byte chunks of this task start on 16-byte boundaries (a
+  // slice-K group may start anywhere).
   __device__ static void load_stage(Stage& st, const GemmArgs& a, const uint8_t* Ab,
                                     const uint8_t* Bb, const Task& tk, uint32_t kb0,
-                                    uint32_t kend, const uint8_t* sab, const uint8_t* sbb) {
+                                    uint32_t kend, const uint8_t* sab, const uint8_t* sbb,
+                                    bool a_al) {
     const uint32_t tid = threadIdx.x;
     const bool k_full = kb0 + T::BK <= kend;
     // Interior stages (the common case) issue every 16-byte load back to
     // back with no predicate; only stages that touch a tail take the masked
     // path.  Both conditions are uniform across the workgroup.
-    if (k_full && tk.rows_valid == (uint32_t)BM) {
+    if (k_full && a_al && tk.rows_valid == (uint32_t)BM) {
 #pragma unroll
       for (int i = 0; i < A_PER_T; ++i) {
         const uint32_t q = tid + i * NT;
@@ -961,11 +1033,15 @@ struct GemmKernel {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
     GroupTable* gt = nullptr;
     uint32_t T_tiles = a.tiles;
-    if constexpr (GROUPED) {
+    if constexpr (FORM != FORM_DENSE) {
       __shared__ GroupTable gtab;
       gt = &gtab;
-      build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
-      T_tiles = gtab.first_task[a.G];
+      if constexpr (FORM == FORM_SLICE_M) {
+        build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
+        T_tiles = gtab.first_task[a.G];
+      } else {
+        build_k_table(gtab, a);
+      }
     }
     const uint32_t units = T_tiles * a.split;
     const uint32_t wave = threadIdx.x >> 6;
@@ -975,15 +1051,23 @@ struct GemmKernel {
     for (uint32_t u = logical_wg(a.remap, a.grid); u < units; u += a.grid) {
       const uint32_t s = u / T_tiles;       // K slice (like GetBatchIdx over slices)
       const uint32_t t = u - s * T_tiles;   // task
-      const Task tk = decode_task(a, t, BM, BN, gt);
-      const uint32_t k0 = s * a.kslice;
-      const uint32_t k1 = (k0 >= a.K || a.K - k0 < a.kslice) ? a.K : k0 + a.kslice;
+      const Task tk = decode_task(a, t, BM, BN, GROUPED ? gt : nullptr);
+      // the task's K range: all of K, or its slice-K group's
+      uint32_t kq = 0, kg = a.K, ks = a.kslice;
+      if constexpr (FORM == FORM_SLICE_K) {
+        kq = (uint32_t)gt->first_row[tk.idx];
+        kg = (uint32_t)gt->first_row[tk.idx + 1] - kq;
+        ks = group_kslice(kg, a.split, T::BK);
+      }
+      const KRange kr = slice_range(kq, kg, ks, s);
+      const uint32_t k0 = kr.k0, k1 = kr.k1;
       const uint32_t klen = k0 < k1 ? k1 - k0 : 0u;
       const uint32_t nk = (klen + T::BK - 1) / T::BK;
+      const bool a_al = FORM != FORM_SLICE_K || (kq * T::ES) % 16u == 0;
 
-      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      const int64_t bidx = FORM == FORM_DENSE ? tk.idx : 0;
       const uint8_t* Ab = a.A + (bidx * a.strideA + tk.row0 * a.lda) * T::ES;
-      const uint8_t* Bb = a.B + ((int64_t)tk.idx * a.strideB) * T::ES;
+      const uint8_t* Bb = a.B + ((int64_t)(FORM == FORM_SLICE_K ? 0 : tk.idx) * a.strideB) * T::ES;
       const uint8_t* sab = a.sa ? a.sa + tk.row0 * a.ldsa : nullptr;
       const uint8_t* sbb = a.sb;
 
@@ -997,14 +1081,14 @@ struct GemmKernel {
 
       if (nk > 0) {
         Stage st;
-        load_stage(st, a, Ab, Bb, tk, k0, k1, sab, sbb);
+        load_stage(st, a, Ab, Bb, tk, k0, k1, sab, sbb, a_al);
         store_stage(st, lds);
         __syncthreads();
         for (uint32_t kt = 0; kt < nk; ++kt) {
           const uint8_t* cur = lds + (kt & 1u) * (STAGE_BYTES + SCALE_BYTES);
           uint8_t* nxt = lds + ((kt + 1) & 1u) * (STAGE_BYTES + SCALE_BYTES);
           const bool more = kt + 1 < nk;
-          if (more) load_stage(st, a, Ab, Bb, tk, k0 + (kt + 1) * T::BK, k1, sab, sbb);
+          if (more) load_stage(st, a, Ab, Bb, tk, k0 + (kt + 1) * T::BK, k1, sab, sbb, a_al);
           compute_stage(acc, cur, wm, wn);
           if (more) store_stage(st, nxt);
           __syncthreads();
@@ -1017,9 +1101,9 @@ struct GemmKernel {
   }
 };
 
-template <int AB, int BM, int BN, int WM, int WN, bool GROUPED>
+template <int AB, int BM, int BN, int WM, int WN, int FORM>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmArgs a) {
-  GemmKernel<AB, BM, BN, WM, WN, GROUPED>::run(a);
+  GemmKernel<AB, BM, BN, WM, WN, FORM>::run(a);
 }
 
 // Map dump: the same scheduler, persistent loop and renumbering as the GEMM

@@ -15,7 +15,7 @@ using LaunchFn = hipError_t (*)(dim3, dim3, hipStream_t, const GemmArgs&);
 struct Instance {
   int ab;  // AbKind
   int bm, bn;
-  bool grouped;
+  int form;    // Form: plain / batched, grouped slice-M, grouped slice-K
   bool dma;    // LDS-DMA family (else register-staged)
   int stages;  // pipeline stages of the LDS-DMA family
   const void* fn;
@@ -30,13 +30,13 @@ struct InstanceList {
   int count;
 };
 
-template <int AB, int BM, int BN, int WM, int WN, bool GR>
+template <int AB, int BM, int BN, int WM, int WN, int GR>
 hipError_t launch_reg(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
   hipLaunchKernelGGL((gemm_kernel<AB, BM, BN, WM, WN, GR>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <int AB, int BM, int BN, int WM, int WN, int S, bool GR, bool ADD = false>
+template <int AB, int BM, int BN, int WM, int WN, int S, int GR, bool ADD = false>
 hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
   hipLaunchKernelGGL((gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR, ADD>), grid, block, 0, st, a);
   return hipGetLastError();
@@ -58,9 +58,9 @@ hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
 // A matmul-add instance of the LDS-DMA family (plain GEMM only).
 #define BST_DMA_ADD(AB, BM, BN, WM, WN, S)                                                \
   Instance {                                                                              \
-    AB, BM, BN, false, true, S,                                                           \
-        reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, false, true>), \
-        &launch_dma<AB, BM, BN, WM, WN, S, false, true>, 64 * WM * WN, Traits<AB>::BK, true \
+    AB, BM, BN, FORM_DENSE, true, S,                                                      \
+        reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, FORM_DENSE, true>), \
+        &launch_dma<AB, BM, BN, WM, WN, S, FORM_DENSE, true>, 64 * WM * WN, Traits<AB>::BK, true \
   }
 
 InstanceList instances_f16();
@@ -68,5 +68,6 @@ InstanceList instances_bf16();
 InstanceList instances_i8();
 InstanceList instances_fp8();
 InstanceList instances_mxfp8();
+InstanceList instances_slicek();
 
 }  // namespace bst

@@ -188,10 +188,11 @@ struct LoopTrace {
 // chunk blocks inside which a B row is permuted.
 constexpr int pow2_block(int n) { return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1; }
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, bool ADD = false>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, int FORM, bool ADD = false>
 struct DmaKernel {
   using T = Traits<AB>;
-  using Epi = Epilogue<AB, BM, BN, WM, WN, GROUPED>;
+  using Epi = Epilogue<AB, BM, BN, WM, WN, FORM>;
+  static constexpr bool GROUPED = FORM == FORM_SLICE_M;
   using Acc = typename Epi::Acc;
   using Frag = typename std::conditional<T::FRAG_DW == 8, i32x8_t, u32x4_t>::type;
   static constexpr int NW = WM * WN, NT = 64 * NW;
@@ -227,7 +228,8 @@ struct DmaKernel {
   static_assert(!T::SCALED || (BM % 64 == 0 && BN % 64 == 0), "whole 256-byte scale instructions");
   static_assert(LPS * STAGES < 64, "vmcnt holds 6 bits");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 MFMA sub-tiles");
-  static_assert(STAGES * STAGE_BYTES <= 160 * 1024 - (GROUPED ? (int)sizeof(GroupTable) : 0) - 16,
+  static_assert(STAGES * STAGE_BYTES <=
+                    160 * 1024 - (FORM != FORM_DENSE ? (int)sizeof(GroupTable) : 0) - 16,
                 "LDS budget");
 
   static __host__ __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
@@ -777,11 +779,15 @@ struct DmaKernel {
 #endif
     GroupTable* gt = nullptr;
     uint32_t T_tiles = a.tiles;
-    if constexpr (GROUPED) {
+    if constexpr (FORM != FORM_DENSE) {
       __shared__ GroupTable gtab;
       gt = &gtab;
-      build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
-      T_tiles = gtab.first_task[a.G];
+      if constexpr (FORM == FORM_SLICE_M) {
+        build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
+        T_tiles = gtab.first_task[a.G];
+      } else {
+        build_k_table(gtab, a);
+      }
     }
     const uint32_t units = T_tiles * a.split;
     Ctx c;
@@ -801,7 +807,7 @@ struct DmaKernel {
     do {
       const uint32_t s = u / T_tiles;
       const uint32_t t = u - s * T_tiles;
-      Task tk = decode_task(a, t, BM, BN, gt);
+      Task tk = decode_task(a, t, BM, BN, GROUPED ? gt : nullptr);
       if constexpr (GROUPED) {
         // the group table lives in LDS: make the task wave-uniform so that
         // the buffer descriptors below stay in scalar registers
@@ -815,12 +821,24 @@ struct DmaKernel {
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tk.row0 >> 32));
         tk.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
       }
-      const uint32_t k0 = s * a.kslice;
-      const uint32_t k1 = (k0 >= a.K || a.K - k0 < a.kslice) ? a.K : k0 + a.kslice;
-      const uint32_t nk = k0 < k1 ? (k1 - k0 + BK - 1) / BK : 0u;
-      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      // the task's K range: all of K, or its slice-K group's
+      uint32_t kq = 0, kg = a.K, ks = a.kslice;
+      if constexpr (FORM == FORM_SLICE_K) {
+        kq = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx]);
+        kg = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx + 1]) - kq;
+        ks = group_kslice(kg, a.split, BK);
+        // A's 16-byte chunks must not straddle a group boundary: a group
+        // that does not start and end on one is not computed, its output
+        // reads NaN (INT32_MIN for raw accumulators)
+        tk.poison = ((kq | kg) % (uint32_t)CE) != 0u;
+      }
+      const KRange kr = slice_range(kq, kg, ks, s);
+      const uint32_t k0 = kr.k0, k1 = kr.k1;
+      const uint32_t nk = (k0 < k1 && !tk.poison) ? (k1 - k0 + BK - 1) / BK : 0u;
+      const int64_t bidx = FORM == FORM_DENSE ? tk.idx : 0;
+      const int64_t bsel = FORM == FORM_SLICE_K ? 0 : tk.idx;
       c.a_tile = a.A + (bidx * a.strideA + tk.row0 * a.lda) * ES;
-      c.b_tile = a.B + ((int64_t)tk.idx * a.strideB + (int64_t)tk.n * BN) * ES;
+      c.b_tile = a.B + (bsel * a.strideB + (int64_t)tk.n * BN) * ES;
       c.sa_tile = T::SCALED ? a.sa + tk.row0 * a.ldsa : nullptr;
       c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
       c.k0 = k0;
@@ -857,10 +875,10 @@ struct DmaKernel {
 };
 
 // ADD: the matmul-add instances (C = A.B + X; plain GEMM only).
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED, bool ADD = false>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, int FORM, bool ADD = false>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only builtins: device pass only
-  DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED, ADD>::run(a);
+  DmaKernel<AB, BM, BN, WM, WN, STAGES, FORM, ADD>::run(a);
 #endif
 }
 

@@ -4,16 +4,16 @@
 namespace bst {
 
 static const Instance kList[] = {
-    BST_REG(AB_BF16, 64, 64, 2, 2, false),  BST_REG(AB_BF16, 128, 128, 2, 2, false),
-    BST_REG(AB_BF16, 256, 128, 2, 2, false), BST_REG(AB_BF16, 128, 256, 2, 2, false),
-    BST_REG(AB_BF16, 128, 192, 2, 2, false), BST_REG(AB_BF16, 128, 128, 2, 2, true),
-    BST_REG(AB_BF16, 128, 64, 2, 2, false),  BST_REG(AB_BF16, 64, 128, 2, 2, false),
-    BST_REG(AB_BF16, 256, 256, 4, 2, false),
-    BST_DMA(AB_BF16, 64, 64, 2, 2, 4, false),  BST_DMA(AB_BF16, 128, 128, 2, 2, 4, false),
-    BST_DMA(AB_BF16, 256, 128, 2, 2, 3, false), BST_DMA(AB_BF16, 128, 256, 2, 2, 3, false),
-    BST_DMA(AB_BF16, 128, 192, 2, 2, 3, false), BST_DMA(AB_BF16, 128, 128, 2, 2, 4, true),
-    BST_DMA(AB_BF16, 256, 256, 4, 2, 2, false),
-    BST_DMA(AB_BF16, 128, 64, 2, 2, 4, false),  BST_DMA(AB_BF16, 64, 128, 2, 2, 4, false),
+    BST_REG(AB_BF16, 64, 64, 2, 2, FORM_DENSE),  BST_REG(AB_BF16, 128, 128, 2, 2, FORM_DENSE),
+    BST_REG(AB_BF16, 256, 128, 2, 2, FORM_DENSE), BST_REG(AB_BF16, 128, 256, 2, 2, FORM_DENSE),
+    BST_REG(AB_BF16, 128, 192, 2, 2, FORM_DENSE), BST_REG(AB_BF16, 128, 128, 2, 2, FORM_SLICE_M),
+    BST_REG(AB_BF16, 128, 64, 2, 2, FORM_DENSE),  BST_REG(AB_BF16, 64, 128, 2, 2, FORM_DENSE),
+    BST_REG(AB_BF16, 256, 256, 4, 2, FORM_DENSE),
+    BST_DMA(AB_BF16, 64, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_BF16, 128, 128, 2, 2, 4, FORM_DENSE),
+    BST_DMA(AB_BF16, 256, 128, 2, 2, 3, FORM_DENSE), BST_DMA(AB_BF16, 128, 256, 2, 2, 3, FORM_DENSE),
+    BST_DMA(AB_BF16, 128, 192, 2, 2, 3, FORM_DENSE), BST_DMA(AB_BF16, 128, 128, 2, 2, 4, FORM_SLICE_M),
+    BST_DMA(AB_BF16, 256, 256, 4, 2, 2, FORM_DENSE),
+    BST_DMA(AB_BF16, 128, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_BF16, 64, 128, 2, 2, 4, FORM_DENSE),
     BST_DMA_ADD(AB_BF16, 64, 64, 2, 2, 4), BST_DMA_ADD(AB_BF16, 128, 128, 2, 2, 4),
 };
 

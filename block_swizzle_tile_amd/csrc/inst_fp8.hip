@@ -4,12 +4,12 @@
 namespace bst {
 
 static const Instance kList[] = {
-    BST_REG(AB_E4M3, 64, 64, 2, 2, false),  BST_REG(AB_E4M3, 128, 128, 2, 2, false),
-    BST_REG(AB_E4M3, 256, 128, 2, 2, false), BST_REG(AB_E4M3, 256, 256, 4, 2, false),
-    BST_REG(AB_E4M3, 128, 64, 2, 2, false),  BST_REG(AB_E4M3, 64, 128, 2, 2, false),
-    BST_DMA(AB_E4M3, 64, 64, 2, 2, 4, false),  BST_DMA(AB_E4M3, 128, 128, 2, 2, 4, false),
-    BST_DMA(AB_E4M3, 256, 128, 2, 2, 3, false), BST_DMA(AB_E4M3, 256, 256, 4, 2, 2, false),
-    BST_DMA(AB_E4M3, 128, 64, 2, 2, 4, false),  BST_DMA(AB_E4M3, 64, 128, 2, 2, 4, false),
+    BST_REG(AB_E4M3, 64, 64, 2, 2, FORM_DENSE),  BST_REG(AB_E4M3, 128, 128, 2, 2, FORM_DENSE),
+    BST_REG(AB_E4M3, 256, 128, 2, 2, FORM_DENSE), BST_REG(AB_E4M3, 256, 256, 4, 2, FORM_DENSE),
+    BST_REG(AB_E4M3, 128, 64, 2, 2, FORM_DENSE),  BST_REG(AB_E4M3, 64, 128, 2, 2, FORM_DENSE),
+    BST_DMA(AB_E4M3, 64, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_E4M3, 128, 128, 2, 2, 4, FORM_DENSE),
+    BST_DMA(AB_E4M3, 256, 128, 2, 2, 3, FORM_DENSE), BST_DMA(AB_E4M3, 256, 256, 4, 2, 2, FORM_DENSE),
+    BST_DMA(AB_E4M3, 128, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_E4M3, 64, 128, 2, 2, 4, FORM_DENSE),
     BST_DMA_ADD(AB_E4M3, 128, 128, 2, 2, 4),
 };
 

@@ -200,6 +200,48 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G,
                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bst_grouped_gemm_slice_k -- G problems that cut one K dimension into
+ * consecutive groups (the grouped-matmul-slice-K example, with and without
+ * per-token dequant, that "Block Dispatch Policies" lists under its
+ * PreloadAsync policies; reading: each group is its own product with its
+ * own output).  Group g owns K indices [Q_g, Q_g + group_k[g]) with Q_g the
+ * sum of the earlier groups' sizes: columns of A (row-major [M][lda],
+ * lda >= total_k) and rows of B (row-major [total_k][ldb]).  Its output is
+ * C_g = A[:, Q_g : Q_g + k_g] . B[Q_g : Q_g + k_g, :], an M x N matrix at
+ * C + g*strideC ([M][ldc]); groups' outputs may not overlap (strideC >=
+ * (M-1)*ldc + N when G > 1, BST_E_INVAL otherwise).  Every group shares M
+ * and N, so the tasks are numbered like the batches of a batched problem
+ * (group of task t = t / tiles per group, s4.4 GetBatchIdx) and
+ * bst_tile_map with batch = G dumps their map.
+ *   group_k_dev: device int32[G] (never read by the host); entries < 0
+ *   count as 0 and a group is cut to the K still left of total_k, so
+ *   nothing past column / row total_k is read.  An empty group's output
+ *   is zeros.  The LDS-DMA kernels (path 2, the automatic choice when the
+ *   layout allows) need every group to start and end on a whole 16-byte
+ *   chunk of A's rows (sizes multiples of 8 for 16-bit operands, 16 for
+ *   int8); a group that does not is not computed and its whole output
+ *   reads NaN (INT32_MIN for raw int32 accumulators), as does every later
+ *   group whose start it shifts.  The register-staged kernels (path 1)
+ *   take groups of any size.
+ *   ab = BST_I8: c = BST_I32 (raw), or BST_BF16 / BST_F16 / BST_F32 with
+ *   optional dequant: with row_scale_dev (f32 [G][M], per group and token
+ *   row) and col_scale_dev (f32 [G][N], per group and channel) both given,
+ *   out = round(float(acc) * row_scale[g][i] * col_scale[g][j]) with each
+ *   product rounded to fp32.  ab = BST_F16 / BST_BF16: no scales.
+ *   1 <= G <= 1024.  The split-K option (sched->split_k) cuts every group's
+ *   K range into that many slices of whole stages on the device (0 = judged
+ *   from the mean group size); ws as for bst_gemm, sized by
+ *   bst_workspace_bytes(3, ab, G, M, N, total_k, sched).
+ */
+bst_status bst_grouped_gemm_slice_k(bst_dtype ab, bst_dtype c, int32_t G,
+                                    const int32_t* group_k_dev, int64_t total_k, int64_t M,
+                                    int64_t N, const void* A_dev, int64_t lda,
+                                    const void* B_dev, int64_t ldb, void* C_dev, int64_t ldc,
+                                    int64_t strideC, const float* row_scale_dev,
+                                    const float* col_scale_dev, const bst_sched* sched,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
  * bst_quant_gemm_per_token -- the quantised matmul with per-token dequant
  * ("Block Dispatch Policies" lists quant-matmul and per-token-dequant
  * examples under its PreloadAsync policies; reading: one problem, the
@@ -246,9 +288,10 @@ bst_status bst_grouped_tile_map(bst_dtype ab, int32_t G, const int32_t* group_m_
 /*
  * bst_workspace_bytes -- workspace bytes a call with these arguments needs
  * (0 when the effective split_k is 1).  kind: 0 plain / batched (count =
- * batch), 1 grouped (count = G, M = total_m), 2 bst_gemm_padded (count 1;
- * the repacked operands plus the split-K workspace, never 0 for a non-empty
- * problem).  Returns 0 and sets the last error for invalid arguments.
+ * batch), 1 grouped slice-M (count = G, M = total_m), 2 bst_gemm_padded
+ * (count 1; the repacked operands plus the split-K workspace, never 0 for a
+ * non-empty problem), 3 grouped slice-K (count = G, K = total_k).  Returns
+ * 0 and sets the last error for invalid arguments.
  */
 size_t bst_workspace_bytes(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                            int64_t K, const bst_sched* sched);
@@ -261,10 +304,10 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
 
 /* bst_task_count -- tasks of the block scheduler for these sizes (s4.3
  * GetCoreLoops times the batch count, s4.4): kind 0 plain / batched
- * (count = batch): exactly count * ceil(M/tile_m) * ceil(N/tile_n); kind 1
- * grouped slice-M (count = G, M = total_m): the bound
- * (ceil(total_m/tile_m) + G) * ceil(N/tile_n), since the group sizes live
- * on the device.  This is the record count bst_tile_map /
+ * (count = batch) and kind 3 grouped slice-K (count = G): exactly
+ * count * ceil(M/tile_m) * ceil(N/tile_n); kind 1 grouped slice-M (count =
+ * G, M = total_m): the bound (ceil(total_m/tile_m) + G) * ceil(N/tile_n),
+ * since the group sizes live on the device.  This is the record count bst_tile_map /
  * bst_grouped_tile_map need.  Tiles are the effective ones (defaults
  * resolved). */
 bst_status bst_task_count(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,

@@ -57,3 +57,18 @@ def check_close(orc, got_tensor, ref, den, tol, what=""):
             what, e, tol, idx, got.reshape(ref.shape)[idx] if idx else None,
             ref[idx] if idx else None, den[idx] if idx else None))
     return e
+
+
+def check_close_rounded(orc, got_tensor, ref, den, tol, unit, what=""):
+    """As check_close for outputs rounded to a format of unit roundoff `unit` (2^-8 for bf16,
+    2^-11 for fp16): the rounding of the result itself, up to unit * |ref|, is allowed on top
+    of tol * den.  A short sum of same-sign terms has |ref| close to den, and then that
+    rounding alone exceeds tol * den."""
+    got = orc.decode(kind_of(got_tensor), codes(got_tensor)).reshape(ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    excess = np.maximum(np.abs(got - ref) - unit * np.abs(ref), 0.0)
+    e = np.where(den > 0, excess / np.where(den > 0, den, 1.0), np.where(got == 0, 0.0, np.inf))
+    at = int(np.argmax(e))
+    assert e.flat[at] <= tol, "%s: normalised error beyond the output rounding %.3g > %.3g at %s" % (
+        what, e.flat[at], tol, np.unravel_index(at, ref.shape))
+    return float(e.flat[at])

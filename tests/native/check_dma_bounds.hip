@@ -44,16 +44,21 @@ struct Problem {
   bool scaled = false;
 };
 
-template <int AB, int BM, int BN, int WM, int WN, int STAGES, bool GROUPED>
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, int FORM>
 void check(const Problem& p) {
-  using KN = DmaKernel<AB, BM, BN, WM, WN, STAGES, GROUPED>;
+  using KN = DmaKernel<AB, BM, BN, WM, WN, STAGES, FORM>;
+  constexpr bool GROUPED = FORM == FORM_SLICE_M;
+  constexpr bool SLICEK = FORM == FORM_SLICE_K;
   constexpr int ES = KN::ES, BK = KN::BK, CE = KN::CE, NW = KN::NW;
-  // schedule: the same split resolution as the host planner (no empty slices)
+  // schedule: the same split resolution as the host planner (no empty
+  // slices); slice-K groups cut their own K on the device, every slice
+  // index up to the requested split exists (slices past a group's end are
+  // empty)
   const int64_t nk_all = (p.K + BK - 1) / BK;
   int64_t split = p.split;
   if (nk_all == 0) split = 1;
   const int64_t ks_steps = nk_all > 0 ? (nk_all + split - 1) / split : 0;
-  if (ks_steps > 0) split = (nk_all + ks_steps - 1) / ks_steps;
+  if (ks_steps > 0 && !SLICEK) split = (nk_all + ks_steps - 1) / ks_steps;
   const uint32_t kslice = (uint32_t)(ks_steps * BK);
 
   GemmArgs a{};
@@ -76,6 +81,11 @@ void check(const Problem& p) {
     fill_group_table(gt, p.groups.data(), a.G, p.M, BM, loopsN);
     gtp = &gt;
     T = gt.first_task[a.G];
+  } else if (SLICEK) {
+    a.G = (int)p.groups.size();
+    a.total_k = p.K;
+    fill_k_table(gt, p.groups.data(), a.G, p.K);
+    T = (uint32_t)(a.G * ((p.M + BM - 1) / BM) * loopsN);
   } else {
     T = (uint32_t)(p.batch * ((p.M + BM - 1) / BM) * loopsN);
   }
@@ -83,9 +93,20 @@ void check(const Problem& p) {
   for (uint32_t s = 0; s < split; ++s) {
     for (uint32_t t = 0; t < T; ++t) {
       const Task tk = decode_task(a, t, BM, BN, gtp);
-      const uint32_t k0 = s * kslice;
-      const uint32_t k1 = (k0 >= a.K || a.K - k0 < kslice) ? a.K : k0 + kslice;
-      const uint32_t nk = k0 < k1 ? (k1 - k0 + BK - 1) / BK : 0u;
+      // the kernel's own K-range code: all of K, or the slice-K group's
+      uint32_t kq = 0, kg = a.K, ks = kslice;
+      bool poison = false;
+      if (SLICEK) {
+        kq = (uint32_t)gt.first_row[tk.idx];
+        kg = (uint32_t)gt.first_row[tk.idx + 1] - kq;
+        ks = group_kslice(kg, (uint32_t)split, BK);
+        poison = ((kq | kg) % (uint32_t)CE) != 0u;
+      }
+      const KRange kr = slice_range(kq, kg, ks, s);
+      const uint32_t k0 = kr.k0, k1 = kr.k1;
+      const uint32_t nk = (k0 < k1 && !poison) ? (k1 - k0 + BK - 1) / BK : 0u;
+      REQUIRE(k1 <= kq + kg && (k0 >= k1 || k0 >= kq), "%s slice [%u,%u) outside group [%u,%u)",
+              p.name.c_str(), k0, k1, kq, kq + kg);
       // valid rows of the tile in the stacked A (group or batch problem)
       int64_t row_lo = tk.row0, row_hi = tk.row0 + tk.rows_valid;
       int64_t prob_rows;  // rows of this problem / group, for the bound check
@@ -97,9 +118,10 @@ void check(const Problem& p) {
         prob_first = 0;
         prob_rows = p.M;
       }
-      const int64_t bidx = GROUPED ? 0 : tk.idx;
+      const int64_t bidx = FORM == FORM_DENSE ? tk.idx : 0;
+      const int64_t bsel = SLICEK ? 0 : tk.idx;
       const int64_t a_tile = (bidx * p.strideA + tk.row0 * p.lda) * ES;  // bytes from A
-      const int64_t b_tile = ((int64_t)tk.idx * p.strideB + (int64_t)tk.n * BN) * ES;
+      const int64_t b_tile = (bsel * p.strideB + (int64_t)tk.n * BN) * ES;
       // a task without partial or padding stages runs the precomputed lane
       // offsets: they must equal the checked ones at every stage
       const bool full = nk > 0 && KN::full_task(k0, k1);
@@ -129,7 +151,10 @@ void check(const Problem& p) {
                           R < prob_first + prob_rows,
                       "%s A row %lld outside [%lld,%lld)", p.name.c_str(), (long long)R,
                       (long long)row_lo, (long long)row_hi);
-              REQUIRE(cb + 16 <= p.K * ES && cb >= (int64_t)kb0 * ES && cb < (int64_t)k1 * ES,
+              // the whole chunk inside the task's K range (a slice-K chunk
+              // may not reach into the next group)
+              REQUIRE(cb + 16 <= p.K * ES && cb >= (int64_t)kb0 * ES &&
+                          cb + 16 <= (int64_t)k1 * ES,
                       "%s A col byte %lld (K %lld, kb0 %u, kend %u)", p.name.c_str(),
                       (long long)cb, (long long)p.K, kb0, k1);
               // coverage: which (row, chunk) of the tile stage landed where
@@ -149,7 +174,7 @@ void check(const Problem& p) {
                 REQUIRE(same(KN::full_voff(ln, KN::A_IPW + i), x.voff), "B full voff");
               if (!x.ok) { REQUIRE(x.voff >= kOob, "disabled B lane in range"); continue; }
               REQUIRE(x.voff < kOob, "B voff %u", x.voff);
-              const int64_t rel = b_tile - (int64_t)tk.idx * p.strideB * ES +
+              const int64_t rel = b_tile - bsel * p.strideB * ES +
                                   (int64_t)kb0 * rowbytesB + x.voff;
               const int64_t R = rel / rowbytesB, cb = rel % rowbytesB;
               REQUIRE(R >= kb0 && R < k1 && R < p.K, "%s B row %lld (kb0 %u kend %u)",
@@ -263,13 +288,32 @@ static Problem grouped(const char* n, std::vector<int32_t> g, int64_t spare, int
   return p;
 }
 
+// Grouped slice-K: K cut into groups of the given sizes (total K = their
+// sum plus `spare` unused columns), M x N outputs.
+static Problem slicek(const char* n, std::vector<int32_t> g, int64_t spare, int64_t M, int64_t N,
+                      uint32_t split) {
+  Problem p;
+  p.name = n;
+  int64_t tot = 0;
+  for (int32_t x : g) tot += x > 0 ? x : 0;
+  p.M = M; p.N = N; p.K = tot + spare;
+  p.lda = p.K; p.ldb = N;
+  p.groups = g;
+  p.split = split;
+  return p;
+}
+
 template <int AB, int BM, int BN, int WM, int WN, int S>
 void run_plain(const std::vector<Problem>& ps) {
-  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, false>(p);
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, FORM_DENSE>(p);
 }
 template <int AB, int BM, int BN, int WM, int WN, int S>
 void run_grouped(const std::vector<Problem>& ps) {
-  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, true>(p);
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, FORM_SLICE_M>(p);
+}
+template <int AB, int BM, int BN, int WM, int WN, int S>
+void run_slicek(const std::vector<Problem>& ps) {
+  for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, FORM_SLICE_K>(p);
 }
 
 int main() {
@@ -295,6 +339,15 @@ int main() {
   run_plain<AB_F16, 64, 64, 2, 2, 6>(p16);
   run_plain<AB_F16, 64, 64, 2, 2, 5>(p16);
   run_grouped<AB_F16, 128, 128, 2, 2, 4>(g16);
+  // slice-K: aligned groups (8 elements), an empty one, a group cut short by
+  // the allocation, and groups that break the 16-byte chunks (no access)
+  const std::vector<Problem> k16 = {slicek("k16", {64, 0, 200, 8, 136}, 16, 129, 264, 1),
+                                    slicek("k16s", {64, 0, 200, 8, 136}, 0, 70, 136, 3),
+                                    slicek("k16bad", {64, 5, 200, 16}, 3, 65, 72, 2),
+                                    slicek("k16big", {1024, 512, 72}, 0, 256, 128, 4)};
+  run_slicek<AB_F16, 64, 64, 2, 2, 4>(k16);
+  run_slicek<AB_F16, 128, 128, 2, 2, 4>(k16);
+  run_slicek<AB_F16, 256, 128, 2, 2, 3>(k16);
   // 8-bit operands: K and N multiples of 16
   const std::vector<Problem> p8 = {
       plain("tails8", 200, 144, 256, 0, 0, 1),   plain("t8split", 333, 528, 384, 16, 16, 3),
@@ -312,6 +365,15 @@ int main() {
   run_grouped<AB_I8, 128, 128, 2, 2, 4>(g8);
   run_grouped<AB_I8, 256, 128, 2, 2, 3>(g8);
   run_grouped<AB_I8, 256, 256, 4, 2, 2>(g8);
+  const std::vector<Problem> k8 = {
+      slicek("k8", {336, 208, 32, 80, 16, 512, 912, 1536}, 0, 200, 144, 1),
+      slicek("k8s", {336, 208, 32, 80, 16, 512, 912, 1536}, 32, 64, 256, 3),
+      slicek("k8e", {0, 0, 48}, 16, 40, 48, 2),
+      slicek("k8bad", {48, 24, 64}, 0, 64, 64, 1)};
+  run_slicek<AB_I8, 64, 64, 2, 2, 4>(k8);
+  run_slicek<AB_I8, 128, 128, 2, 2, 4>(k8);
+  run_slicek<AB_I8, 256, 128, 2, 2, 3>(k8);
+  run_slicek<AB_I8, 256, 256, 4, 2, 2>(k8);
   // fp8: plain (no scales; their kernels issue no scale DMA) and MX (K a
   // multiple of 128, scales always present)
   run_plain<AB_E4M3, 64, 64, 2, 2, 4>(p8);

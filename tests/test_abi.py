@@ -257,3 +257,42 @@ def test_quant_requires_scales(L):
     r = L.bst_quant_gemm_per_token(64, 64, 64, FAKE, 64, FAKE, 64, None, None, FAKE2, 64,
                                    _lib.BF16, None, None, 0, None)
     assert r == _lib.E_INVAL
+
+
+def test_slice_k_validation(L):
+    """bst_grouped_gemm_slice_k: validation before any launch."""
+    def call(G=4, gk=FAKE, total_k=256, M=64, N=64, ab=_lib.I8, c=_lib.I32, lda=None, ldc=64,
+             strideC=None, rs=None, cs=None, A=FAKE, C=FAKE2, sched=None, ws=None, wsb=0):
+        lda = total_k if lda is None else lda
+        strideC = M * ldc if strideC is None else strideC
+        return L.bst_grouped_gemm_slice_k(ab, c, G, gk, total_k, M, N, A, lda, FAKE, N, C, ldc,
+                                          strideC, rs, cs,
+                                          None if sched is None else ctypes.byref(sched), ws,
+                                          wsb, None)
+    assert call(G=0) == _lib.E_INVAL
+    assert call(G=1025) == _lib.E_INVAL
+    assert call(gk=None) == _lib.E_INVAL
+    assert call(rs=FAKE) == _lib.E_INVAL                 # one scale without the other
+    assert call(rs=FAKE, cs=FAKE) == _lib.E_INVAL        # dequant into int32
+    assert call(ab=_lib.E4M3, c=_lib.BF16) == _lib.E_UNSUPPORTED
+    assert call(ab=_lib.MXE4M3, c=_lib.BF16) == _lib.E_UNSUPPORTED
+    assert call(ab=_lib.F16, c=_lib.I32) == _lib.E_UNSUPPORTED
+    assert call(lda=200) == _lib.E_INVAL                 # lda < total_k
+    assert call(ldc=32) == _lib.E_INVAL                  # ldc < N
+    assert call(strideC=63 * 64 + 63) == _lib.E_INVAL    # outputs of groups overlap
+    assert call(A=None) == _lib.E_INVAL
+    assert call(C=ODD) == _lib.E_ALIGN
+    assert call(lda=260) == _lib.E_ALIGN                 # 260-byte int8 rows
+    assert call(M=0, C=None) == _lib.OK                  # no output
+    s = S(tile=(128, 128), split_k=4)
+    need = L.bst_workspace_bytes(3, _lib.I8, 4, 64, 64, 256, ctypes.byref(s))
+    assert need == 65536 + 4 * 4 * 128 * 128 * 4         # 4 groups x 1 tile x 4 slices
+    assert call(sched=s) == _lib.E_WORKSPACE
+    assert call(sched=S(tile=(96, 96))) == _lib.E_UNSUPPORTED
+    n = ctypes.c_int64(-1)
+    assert L.bst_task_count(3, _lib.I8, 8, 1024, 2048, ctypes.byref(S(tile=(256, 256))),
+                            ctypes.byref(n)) == _lib.OK and n.value == 8 * 4 * 8
+    out = _lib.Sched()
+    assert L.bst_effective_sched(3, _lib.I8, 8, 1024, 2048, 8192,
+                                 ctypes.byref(S(tile=(256, 256))), ctypes.byref(out)) == _lib.OK
+    assert out.path == 2 and out.split_k == 1

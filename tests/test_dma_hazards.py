@@ -25,7 +25,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_swizzle_tile_amd", "csrc")
 OBJ = os.path.join(ROOT, "block_swizzle_tile_amd", "_build")
 LLVM = "/opt/rocm/llvm/bin"
-TUS = ["inst_f16.hip", "inst_bf16.hip", "inst_i8.hip", "inst_fp8.hip", "inst_mxfp8.hip"]
+TUS = ["inst_f16.hip", "inst_bf16.hip", "inst_i8.hip", "inst_fp8.hip", "inst_mxfp8.hip",
+       "inst_slicek.hip"]
 DEPS = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "bst.h")]
 
 
