@@ -29,7 +29,7 @@ EXPORTS = ["bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
 class Sched(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in
                 ("tile_m", "tile_n", "tile_k", "swizzle_offset", "swizzle_direction", "split_k",
-                 "xcd_remap", "grid", "path", "shuffle_k")]
+                 "xcd_remap", "grid", "path", "shuffle_k", "dynamic", "preload")]
 
 
 _lock = threading.Lock()
@@ -43,6 +43,11 @@ def lib():
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError("libbst.so is not built (%s); run "
                                    "`python -m block_swizzle_tile_amd.build`" % LIB_PATH)
+            # torch carries its own HIP runtime under the soname libamdhip64.so.7, the same
+            # as the system one libbst.so links: whichever loads first serves the process.
+            # torch is loaded first so that it keeps its own (loading libbst.so first binds
+            # the system runtime, and torch then finds no GPU).
+            import torch  # noqa: F401
             L = ctypes.CDLL(LIB_PATH)
             i64, i32, p, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
             sz, sp = ctypes.c_size_t, ctypes.POINTER(Sched)

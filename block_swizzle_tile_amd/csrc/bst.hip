@@ -111,17 +111,20 @@ int occupancy(const Instance* in) {
 
 // ------------------------------------------------------------ planning ----
 constexpr int64_t kMaxU32 = 0x7fffffffLL;
-// Workspace layout: a fixed counter area (one arrival counter per tile) that
-// partial tiles never overwrite, then the fp32 / int32 partial tiles.  The
-// counter area must be zero before the first call; every call leaves the
-// counters it used at zero, whatever its tile count or split.
+// Workspace layout: a fixed counter area that partial tiles never
+// overwrite -- one arrival counter per tile, then the dynamic allocation's
+// eight queue counters and exit count -- followed by the fp32 / int32
+// partial tiles.  The counter area must be zero before the first call;
+// every call leaves the counters it used at zero, whatever its tile count,
+// split or allocation.
 constexpr uint32_t kMaxSplitTiles = 16384;
-constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
+constexpr size_t kQueueOffset = kMaxSplitTiles * 4;
+constexpr size_t kCounterBytes = kQueueOffset + 8192;  // 57 counters, one per 128-byte line
 
 struct Plan {
   const Instance* inst = nullptr;
   uint32_t bm = 0, bn = 0, bk = 0;
-  uint32_t off = 1, dir = 0, remap = 0, shuffle = 0;
+  uint32_t off = 1, dir = 0, remap = 0, shuffle = 0, dynamic = 0, preload = 0;
   uint32_t split = 1, kslice = 0;
   uint64_t tile_cap = 0;  // tiles (upper bound for grouped)
   uint32_t grid = 0;
@@ -187,6 +190,8 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
   }
   if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
   if (d.shuffle_k > 1) return fail(BST_E_INVAL, "shuffle_k must be 0 or 1");
+  if (d.dynamic > 1) return fail(BST_E_INVAL, "dynamic must be 0 or 1");
+  if (d.preload > 1) return fail(BST_E_INVAL, "preload must be 0 or 1");
   // matmul-add runs only the LDS-DMA instances built with the addend epilogue
   const Instance* reg = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, form, false);
   const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, form, true, add);
@@ -215,7 +220,12 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
   p.off = d.swizzle_offset;
   p.dir = d.swizzle_direction;
   p.remap = d.xcd_remap;
-  p.shuffle = p.inst->dma ? d.shuffle_k : 0u;  // the register-staged family runs stages in order
+  // ShuffleK, dynamic allocation and preload are LDS-DMA features; the
+  // register-staged family runs stages in order over a static stride
+  p.shuffle = p.inst->dma ? d.shuffle_k : 0u;
+  p.dynamic = p.inst->dma ? d.dynamic : 0u;
+  // with dynamic allocation the next task is known only after the epilogue
+  p.preload = (p.inst->dma && !p.dynamic) ? d.preload : 0u;
   const int64_t loopsN = cdiv64(N, p.bn);
   const int64_t tiles = form == FORM_SLICE_M ? (cdiv64(M, p.bm) + count) * loopsN
                                              : count * cdiv64(M, p.bm) * loopsN;
@@ -246,6 +256,8 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
                   (long long)tiles);
     p.part_bytes = (size_t)p.split * (size_t)tiles * p.bm * p.bn * 4;
     p.ws_bytes = kCounterBytes + p.part_bytes;
+  } else if (p.dynamic) {
+    p.ws_bytes = kCounterBytes;  // the queue counters
   }
   const int64_t units = tiles * split;
   int64_t grid = d.grid;
@@ -267,8 +279,9 @@ bool stride_ok(int64_t ld, size_t es) { return ((uint64_t)ld * es) % 16 == 0; }
 bst_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
   if (p.ws_bytes == 0) return BST_OK;
   if (!ws || ws_bytes < p.ws_bytes)
-    return fail(BST_E_WORKSPACE, "split %u needs %zu workspace bytes (got %zu)", p.split,
-                p.ws_bytes, ws ? ws_bytes : (size_t)0);
+    return fail(BST_E_WORKSPACE, "split %u%s needs %zu workspace bytes (got %zu)", p.split,
+                p.dynamic ? " with dynamic allocation" : "", p.ws_bytes,
+                ws ? ws_bytes : (size_t)0);
   if (!aligned16(ws)) return fail(BST_E_ALIGN, "workspace not 16-byte aligned");
   return BST_OK;
 }
@@ -279,10 +292,13 @@ void fill_ws(GemmArgs& a, const Plan& p, void* ws) {
   a.tile_cap = (uint32_t)p.tile_cap;
   a.ws_part = nullptr;
   a.ws_count = nullptr;
+  a.queue = nullptr;
+  a.preload = p.preload;
   if (p.split > 1) {
     a.ws_count = reinterpret_cast<uint32_t*>(ws);
     a.ws_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
   }
+  if (p.dynamic) a.queue = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kQueueOffset);
 }
 
 bst_status launch(const Plan& p, const GemmArgs& a, void* stream) {
@@ -785,6 +801,8 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
   out->grid = p.grid;
   out->path = p.inst->dma ? 2u : 1u;
   out->shuffle_k = p.shuffle;
+  out->dynamic = p.dynamic;
+  out->preload = p.preload;
   return BST_OK;
 }
 

@@ -80,6 +80,9 @@ struct GemmArgs {
   uint32_t kslice;                    // K elements per slice (multiple of the stage depth)
   uint32_t remap;                     // XCD-contiguous renumbering of workgroups
   uint32_t shuffle_k;                 // rotate each whole-stage task's K-loop start (ShuffleK)
+  uint32_t preload;                   // issue the next unit's first stages before the epilogue
+  uint32_t* queue;                    // dynamic task allocation: 8 queue counters + exit count
+                                      // (null: static stride)
   uint32_t grid;                      // workgroups launched (gridDim.x, passed here because the
                                       // kernel would read it from the dispatch packet in host
                                       // memory: about a microsecond at every kernel start)

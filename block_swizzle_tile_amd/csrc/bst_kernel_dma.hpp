@@ -671,17 +671,32 @@ struct DmaKernel {
     });
   }
 
+  // The first stage of a task, into buffer 0, issued ahead of its K loop
+  // while the previous task's epilogue runs (which stages through buffer
+  // STAGES-1).
+  template <bool FULL>
+  __device__ static __forceinline__ void preload_stage0(const Ctx& c) {
+    const Dma d = make_dma<FULL>(c);
+    issue<0, FULL>(c, d, stage_k(c, 0));
+  }
+
   // The K loop of one task: nkp (padded, >= UNR) stages from K index c.k0.
+  // pre: stage 0 was issued ahead (preload_stage0).  The epilogue stores
+  // issued after it count in vmcnt too; the first wait still allows only
+  // the stages issued here to stay in flight, so it covers stage 0 (and the
+  // stores, in whatever order they complete).
   template <bool FULL>
   __device__ static __forceinline__ void kloop(Acc (&acc)[FM][FN], const Ctx& c, uint32_t nkp,
-                                               uint32_t wm, uint32_t wn, uint64_t* trace_out) {
+                                               uint32_t wm, uint32_t wn, uint64_t* trace_out,
+                                               bool pre) {
     LoopTrace tr;
     tr.begin();
     const Dma d = make_dma<FULL>(c);
     uint32_t kt = 0;
     if constexpr (STAGES > 2) {
       // stages 0..STAGES-2 in flight, then stage 0 resident
-      static_for<STAGES - 1>([&](auto i) {
+      if (!pre) issue<0, FULL>(c, d, stage_k(c, 0));
+      static_for_range<1, STAGES - 1>([&](auto i) {
         constexpr int I = decltype(i)::value;
         issue<I, FULL>(c, d, stage_k(c, I));
       });
@@ -711,7 +726,7 @@ struct DmaKernel {
         step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr);
       });
     } else {
-      issue<0, FULL>(c, d, stage_k(c, 0));
+      if (!pre) issue<0, FULL>(c, d, stage_k(c, 0));
       tr.prologue_done();
       for (; kt + STAGES < nkp; kt += STAGES) {
         step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
@@ -728,47 +743,133 @@ struct DmaKernel {
     tr.finish(trace_out);
   }
 
-  // One task: K loop (if any), split-K fix-up, epilogue.
-  template <bool FULL>
-  __device__ static __forceinline__ void task(const GemmArgs& a, const Ctx& c, const Task& tk,
-                                              uint32_t s, uint32_t t, uint32_t nk, uint32_t wm,
-                                              uint32_t wn, uint64_t t_start) {
-    const uint64_t t_loop = trace_stamp();
-    Acc acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-    if (nk > 0) kloop<FULL>(acc, c, padded_stages(nk), wm, wn, a.trace);
-    const uint64_t t_epi = trace_stamp();
-    uint64_t t_fix = t_epi;
-    if (Epi::fixup(a, acc, s, t)) {
-      t_fix = trace_stamp();
-      Epi::template store_tile<STAGE_BYTES, ADD>(a, tk, acc, wm, wn,
-                                                 stage_buf<0, STAGE_BYTES>());
+  // One work unit (a K slice of a task) as the persistent loop sees it.
+  struct Unit {
+    Task tk;
+    uint32_t s, t;  // K slice, task
+    uint32_t nk;    // stages (0: nothing to load)
+    bool whole;     // no partial or padding stage: precomputed DMA offsets
+  };
+
+  // Decodes unit u and fills the per-task part of the DMA context.
+  __device__ static __forceinline__ void setup_unit(const GemmArgs& a, const GroupTable* gt,
+                                                    uint32_t T_tiles, uint32_t u, Unit& un,
+                                                    Ctx& c) {
+    un.s = u / T_tiles;
+    un.t = u - un.s * T_tiles;
+    Task tk = decode_task(a, un.t, BM, BN, GROUPED ? gt : nullptr);
+    if constexpr (GROUPED) {
+      // the group table lives in LDS: make the task wave-uniform so that
+      // the buffer descriptors below stay in scalar registers
+      tk.idx = __builtin_amdgcn_readfirstlane(tk.idx);
+      tk.m = __builtin_amdgcn_readfirstlane(tk.m);
+      tk.n = __builtin_amdgcn_readfirstlane(tk.n);
+      tk.mAct = __builtin_amdgcn_readfirstlane(tk.mAct);
+      tk.nAct = __builtin_amdgcn_readfirstlane(tk.nAct);
+      tk.rows_valid = __builtin_amdgcn_readfirstlane(tk.rows_valid);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)tk.row0);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tk.row0 >> 32));
+      tk.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
     }
-#ifdef BST_TRACE
-    const uint64_t t_end = trace_stamp();
-    __builtin_amdgcn_s_waitcnt(0);
-    const uint64_t t_done = trace_stamp();
-    if (a.trace != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
-      uint64_t* o = a.trace + 32 + (threadIdx.x >> 6) * 4;
-      o[0] += t_loop - t_start;  // task setup (first task: from kernel start)
-      o[1] += t_epi - t_loop;    // K loop
-      o[2] += t_end - t_epi;     // fix-up and epilogue
-      o[3] += 1;                 // tasks
-      uint64_t* q = a.trace + 64 + (threadIdx.x >> 6) * 4;
-      q[0] += t_fix - t_epi;     // fix-up
-      q[1] += t_end - t_fix;     // stores issued
-      q[2] += t_done - t_end;    // stores complete
+    // the task's K range: all of K, or its slice-K group's
+    uint32_t kq = 0, kg = a.K, ks = a.kslice;
+    if constexpr (FORM == FORM_SLICE_K) {
+      kq = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx]);
+      kg = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx + 1]) - kq;
+      ks = group_kslice(kg, a.split, BK);
+      // A's 16-byte chunks must not straddle a group boundary: a group
+      // that does not start and end on one is not computed, its output
+      // reads NaN (INT32_MIN for raw accumulators)
+      tk.poison = ((kq | kg) % (uint32_t)CE) != 0u;
     }
-#else
-    (void)t_start;
-    (void)t_loop;
-    (void)t_epi;
-#endif
+    const KRange kr = slice_range(kq, kg, ks, un.s);
+    const uint32_t k0 = kr.k0, k1 = kr.k1;
+    un.nk = (k0 < k1 && !tk.poison) ? (k1 - k0 + BK - 1) / BK : 0u;
+    const int64_t bidx = FORM == FORM_DENSE ? tk.idx : 0;
+    const int64_t bsel = FORM == FORM_SLICE_K ? 0 : tk.idx;
+    c.a_tile = a.A + (bidx * a.strideA + tk.row0 * a.lda) * ES;
+    c.b_tile = a.B + (bsel * a.strideB + (int64_t)tk.n * BN) * ES;
+    c.sa_tile = T::SCALED ? a.sa + tk.row0 * a.ldsa : nullptr;
+    c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
+    c.k0 = k0;
+    c.kend = k1;
+    un.whole = un.nk > 0 && full_task(k0, k1);
+    c.kshift = (a.shuffle_k != 0 && un.whole) ? un.t % un.nk : 0u;
+    c.nks = (a.shuffle_k != 0 && un.whole) ? un.nk : 0xFFFFFFFFu;
+    lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
+               c.ldb_bytes, a.ldsa, a.ldsb);
+    un.tk = tk;
+  }
+
+  // Dynamic task allocation ("Block Scheduler Code Explained", s1, names it
+  // among the scheduler's policies): the first round of units, one per
+  // workgroup, is assigned as in the static stride; the rest are split into
+  // eight contiguous ranges, one queue per XCD.  A workgroup takes tickets
+  // (device-scope atomic increments of its queue's counter) from the queue
+  // of the XCD it runs on, then from the others in turn, so the work of a
+  // slow or short-staffed XCD is taken over.  Only the order in which
+  // workgroups meet the units changes: each unit computes exactly what it
+  // computes under the static stride.  Thread 0 of a workgroup holds its
+  // queue and ticket.  A ticket is requested when a unit's K loop ends, not
+  // before it starts: a wave's vector-memory results return in order, so an
+  // atomic in flight ahead of the stage loads would hold them back, while
+  // after the loop its latency overlaps the fix-up and the epilogue.
+  //
+  // Counter area: one counter per 128-byte line (device-scope atomics on
+  // one line are served one at a time): lines 0-7 the queues, line 8 the
+  // count of exit groups done, lines 9.. one exit count per group of at
+  // least 32 workgroups (counting all exits on one word would serialise
+  // every workgroup's exit).  The last workgroup of each group bumps line
+  // 8, and the last group's last workgroup sets every counter back to zero
+  // for the next call in stream order.
+  struct Queues {
+    uint32_t first, count;  // dynamic units: [first, first + count)
+    __device__ __forceinline__ uint32_t lo(uint32_t x) const {
+      return first + x * (count / kNumXcd) + (x < count % kNumXcd ? x : count % kNumXcd);
+    }
+    __device__ __forceinline__ uint32_t len(uint32_t x) const {
+      return count / kNumXcd + (x < count % kNumXcd ? 1u : 0u);
+    }
+  };
+  static constexpr uint32_t kNoUnit = 0xFFFFFFFFu;
+  static constexpr uint32_t kLine = 32;  // uint32 words per 128-byte line
+  static constexpr uint32_t kGroupsDone = 8 * kLine, kGroupBase = 9 * kLine, kMaxExitGroups = 48;
+
+  // Thread 0: the unit the held ticket of queue q stands for, or the next
+  // queue's, ...; kNoUnit once every queue is spent.  q is left on the queue
+  // the unit came from.
+  __device__ static __forceinline__ uint32_t take(const GemmArgs& a, const Queues& Q, uint32_t& q,
+                                                  uint32_t ticket) {
+    for (uint32_t tries = 0;; ++tries) {
+      if (ticket < Q.len(q)) return Q.lo(q) + ticket;
+      if (tries + 1 == (uint32_t)kNumXcd) return kNoUnit;
+      q = (q + 1) % kNumXcd;
+      ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // Thread 0, once its workgroup has no unit left: the exit count, and the
+  // reset by the last workgroup out.
+  __device__ static __forceinline__ void queue_exit(const GemmArgs& a) {
+    const uint32_t G = a.grid;
+    uint32_t gsz = (G + kMaxExitGroups - 1) / kMaxExitGroups;
+    if (gsz < 32u) gsz = 32u;
+    const uint32_t ngroups = (G + gsz - 1) / gsz;
+    const uint32_t grp = blockIdx.x / gsz;
+    const uint32_t members = (grp + 1 == ngroups) ? G - grp * gsz : gsz;
+    const uint32_t in_grp = __hip_atomic_fetch_add(&a.queue[kGroupBase + grp * kLine], 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (in_grp + 1 != members) return;
+    const uint32_t done = __hip_atomic_fetch_add(&a.queue[kGroupsDone], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (done + 1 != ngroups) return;
+    for (uint32_t x = 0; x < (uint32_t)kNumXcd; ++x)
+      __hip_atomic_store(&a.queue[x * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.queue[kGroupsDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t g = 0; g < ngroups; ++g)
+      __hip_atomic_store(&a.queue[kGroupBase + g * kLine], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
@@ -797,64 +898,103 @@ struct DmaKernel {
     c.ldb_bytes32 = (uint32_t)c.ldb_bytes;
     c.ldsb32 = (uint32_t)a.ldsb;
     const uint32_t wm = c.wave / WN, wn = c.wave % WN;
+    // dynamic allocation, when there are units past the first round
+    const Queues Q{a.grid, units > a.grid ? units - a.grid : 0u};
+    const bool dyn = a.queue != nullptr && Q.count > 0;
+    const bool preload = !dyn && a.preload != 0;
+    uint32_t q = xcc_id(), ticket = 0;  // thread 0's queue and held ticket
+    // thread 0 publishes the next unit here, alternating slots, so that a
+    // slot is rewritten only after a later barrier that every wave passed
+    // after reading it
+    __shared__ uint32_t next_unit[2];
+    uint32_t round = 0;
 
     // The host launches at most one workgroup per unit, so a plain launch's
-    // first unit exists and the loop needs no test before it (which lets the
-    // compiler issue the kernel-argument loads as one batch); a grouped
-    // launch learns its task count here on the device.
+    // first unit exists (a grouped launch learns its unit count here).
     uint32_t u = logical_wg(a.remap, a.grid);
-    if (GROUPED && u >= units) return;
-    do {
-      const uint32_t s = u / T_tiles;
-      const uint32_t t = u - s * T_tiles;
-      Task tk = decode_task(a, t, BM, BN, GROUPED ? gt : nullptr);
-      if constexpr (GROUPED) {
-        // the group table lives in LDS: make the task wave-uniform so that
-        // the buffer descriptors below stay in scalar registers
-        tk.idx = __builtin_amdgcn_readfirstlane(tk.idx);
-        tk.m = __builtin_amdgcn_readfirstlane(tk.m);
-        tk.n = __builtin_amdgcn_readfirstlane(tk.n);
-        tk.mAct = __builtin_amdgcn_readfirstlane(tk.mAct);
-        tk.nAct = __builtin_amdgcn_readfirstlane(tk.nAct);
-        tk.rows_valid = __builtin_amdgcn_readfirstlane(tk.rows_valid);
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)tk.row0);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tk.row0 >> 32));
-        tk.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
+    bool have = !GROUPED || u < units;
+    bool pre = false;  // the unit's first stages were issued ahead
+    Unit un;
+    if (have) setup_unit(a, gt, T_tiles, u, un, c);
+    while (have) {
+      const uint64_t t_loop = trace_stamp();
+      Acc acc[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+      if (un.nk > 0) {
+        if (un.whole)
+          kloop<true>(acc, c, padded_stages(un.nk), wm, wn, a.trace, pre);
+        else
+          kloop<false>(acc, c, padded_stages(un.nk), wm, wn, a.trace, pre);
       }
-      // the task's K range: all of K, or its slice-K group's
-      uint32_t kq = 0, kg = a.K, ks = a.kslice;
-      if constexpr (FORM == FORM_SLICE_K) {
-        kq = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx]);
-        kg = __builtin_amdgcn_readfirstlane((uint32_t)gt->first_row[tk.idx + 1]) - kq;
-        ks = group_kslice(kg, a.split, BK);
-        // A's 16-byte chunks must not straddle a group boundary: a group
-        // that does not start and end on one is not computed, its output
-        // reads NaN (INT32_MIN for raw accumulators)
-        tk.poison = ((kq | kg) % (uint32_t)CE) != 0u;
+      const uint64_t t_epi = trace_stamp();
+      if (dyn && threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = Epi::fixup(a, acc, un.s, un.t);
+      const uint64_t t_fix = trace_stamp();
+      // static stride: the next unit is known now, and with preload its
+      // first stage goes out before this unit's epilogue, whose staging
+      // uses a buffer the stage does not.  Only the unit index is kept across
+      // the epilogue (its set-up is redone after it), so that the
+      // epilogue's registers stay its own.
+      uint32_t nu = dyn ? kNoUnit : u + a.grid;
+      pre = false;
+      if (preload && nu < units) {
+        Unit nx;
+        Ctx cn = c;
+        setup_unit(a, gt, T_tiles, nu, nx, cn);
+        if (nx.nk > 0) {
+          if (nx.whole)
+            preload_stage0<true>(cn);
+          else
+            preload_stage0<false>(cn);
+          pre = true;
+        }
       }
-      const KRange kr = slice_range(kq, kg, ks, s);
-      const uint32_t k0 = kr.k0, k1 = kr.k1;
-      const uint32_t nk = (k0 < k1 && !tk.poison) ? (k1 - k0 + BK - 1) / BK : 0u;
-      const int64_t bidx = FORM == FORM_DENSE ? tk.idx : 0;
-      const int64_t bsel = FORM == FORM_SLICE_K ? 0 : tk.idx;
-      c.a_tile = a.A + (bidx * a.strideA + tk.row0 * a.lda) * ES;
-      c.b_tile = a.B + (bsel * a.strideB + (int64_t)tk.n * BN) * ES;
-      c.sa_tile = T::SCALED ? a.sa + tk.row0 * a.ldsa : nullptr;
-      c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
-      c.k0 = k0;
-      c.kend = k1;
-      const bool whole = nk > 0 && full_task(k0, k1);
-      c.kshift = (a.shuffle_k != 0 && whole) ? t % nk : 0u;
-      c.nks = (a.shuffle_k != 0 && whole) ? nk : 0xFFFFFFFFu;
-      lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
-                 c.ldb_bytes, a.ldsa, a.ldsb);
-      if (whole)
-        task<true>(a, c, tk, s, t, nk, wm, wn, t_start);
-      else
-        task<false>(a, c, tk, s, t, nk, wm, wn, t_start);
+      if (last)
+        Epi::template store_tile<STAGE_BYTES, ADD>(a, un.tk, acc, wm, wn,
+                                                   stage_buf<STAGES - 1, STAGE_BYTES>());
+      if (dyn) {
+        if (threadIdx.x == 0) next_unit[round & 1u] = take(a, Q, q, ticket);
+        __syncthreads();
+        nu = __builtin_amdgcn_readfirstlane(next_unit[round & 1u]);
+        ++round;
+      }
+      have = nu < units;
+#ifdef BST_TRACE
+      {
+        const uint64_t t_end = trace_stamp();
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint64_t t_done = trace_stamp();
+        if (a.trace != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
+          uint64_t* o = a.trace + 32 + (threadIdx.x >> 6) * 4;
+          o[0] += t_loop - t_start;  // unit set-up (first unit: from kernel start)
+          o[1] += t_epi - t_loop;    // K loop
+          o[2] += t_end - t_epi;     // fix-up, preload, epilogue, next ticket
+          o[3] += 1;                 // units
+          uint64_t* r = a.trace + 64 + (threadIdx.x >> 6) * 4;
+          r[0] += t_fix - t_epi;     // fix-up
+          r[1] += t_end - t_fix;     // preload, stores issued, next ticket
+          r[2] += t_done - t_end;    // stores complete
+        }
+      }
+#else
+      (void)t_loop;
+      (void)t_epi;
+      (void)t_fix;
+#endif
+      if (have) {
+        setup_unit(a, gt, T_tiles, nu, un, c);
+        u = nu;
+      }
       t_start = trace_stamp();
-      u += a.grid;
-    } while (u < units);
+    }
+    if (dyn && threadIdx.x == 0) queue_exit(a);
 #ifdef BST_TRACE
     // Clock record of the first 256 workgroups at trace[128 + 4 w]: the
     // 100 MHz reference counter at the start and at the end, and the shader

@@ -86,6 +86,21 @@ typedef struct bst_sched {
                                   LDS-DMA family to tasks of whole stages; others run in order.
                                   0 = off.  Results differ from 0 only by fp32 summation order
                                   (int8: bit-identical). */
+  uint32_t dynamic;            /* 1: dynamic task allocation ("Block Scheduler Code Explained",
+                                  s1): after a first round of one unit per workgroup, the
+                                  units go to eight queues, one per XCD; each workgroup takes
+                                  tickets from its own XCD's queue, then from the others, so
+                                  uneven tiles and groups even out.  Needs the workspace's
+                                  counter area (bst_workspace_bytes is never 0 with it).
+                                  LDS-DMA family only; results are identical to 0.
+                                  0 = static stride. */
+  uint32_t preload;            /* 1: block preloading (a policy of the Preload dispatch
+                                  policies, "Block Dispatch Policies"): a workgroup issues the
+                                  first stage of its next task before the current task's
+                                  epilogue, which stages through a buffer it does not use.
+                                  LDS-DMA family with the static stride only (with dynamic
+                                  allocation the next task is known only after the
+                                  epilogue); results are identical to 0. */
 } bst_sched;
 
 /*
@@ -105,12 +120,13 @@ typedef struct bst_sched {
  *   the block's products).
  *   Accumulation is fp32 (int32 for int8); outputs are rounded to nearest
  *   even.  ws / ws_bytes: workspace of at least bst_workspace_bytes(...)
- *   bytes when the (possibly automatic) split_k is above 1, else may be
- *   NULL / 0.  Layout: a 64 KiB counter area (one uint32 per tile, at most
- *   16384 tiles take a split) followed by the partial tiles.  The counter
- *   area must be zero before the first use of a workspace; every call that
- *   runs to completion leaves it zero again, so one workspace serves calls
- *   of any shape in stream order.
+ *   bytes when the (possibly automatic) split_k is above 1 or dynamic
+ *   allocation is on, else may be NULL / 0.  Layout: a counter area of
+ *   73728 bytes (one uint32 per tile, at most 16384 tiles take a split;
+ *   then 8 KiB of work-queue counters) followed by the partial tiles.
+ *   The counter area must be zero before the first use of a workspace;
+ *   every call that runs to completion leaves it zero again, so one
+ *   workspace serves calls of any shape in stream order.
  */
 bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
                     const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,

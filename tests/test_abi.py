@@ -94,7 +94,7 @@ def test_empty_problems_are_noops(L):
 def test_workspace_required_for_split(L):
     s = S(tile=(128, 128), split_k=4)
     need = L.bst_workspace_bytes(0, _lib.F16, 1, 1024, 1024, 2048, ctypes.byref(s))
-    assert need == 65536 + 4 * 64 * 128 * 128 * 4
+    assert need == 73728 + 4 * 64 * 128 * 128 * 4
     assert gemm(L, M=1024, N=1024, K=2048, sched=s) == _lib.E_WORKSPACE
     assert gemm(L, M=1024, N=1024, K=2048, sched=s, ws=FAKE, wsb=need - 1) == _lib.E_WORKSPACE
     assert L.bst_workspace_bytes(0, _lib.F16, 1, 1024, 1024, 2048,
@@ -142,9 +142,9 @@ def test_gemm_add_validation(L):
 def test_gemm_padded_validation(L):
     """bst_gemm_padded: workspace sizing and validation before any launch."""
     need = L.bst_workspace_bytes(2, _lib.F16, 1, 64, 64, 60, None)
-    # 64 KiB counter area, then A 64 x 64 and B 64 x 64 fp16: rows padded to 16 bytes and
+    # 73728-byte counter area, then A 64 x 64 and B 64 x 64 fp16: rows padded to 16 bytes and
     # B's K padded the same way (4 zero rows)
-    assert need == 65536 + 64 * 64 * 2 + 64 * 64 * 2
+    assert need == 73728 + 64 * 64 * 2 + 64 * 64 * 2
     assert L.bst_workspace_bytes(3, _lib.F16, 1, 64, 64, 60, None) == 0   # no such kind
 
     def pad(ws=None, wsb=0, ab=_lib.F16, c=_lib.F16, sa=None, sb=None, **kw):
@@ -286,7 +286,7 @@ def test_slice_k_validation(L):
     assert call(M=0, C=None) == _lib.OK                  # no output
     s = S(tile=(128, 128), split_k=4)
     need = L.bst_workspace_bytes(3, _lib.I8, 4, 64, 64, 256, ctypes.byref(s))
-    assert need == 65536 + 4 * 4 * 128 * 128 * 4         # 4 groups x 1 tile x 4 slices
+    assert need == 73728 + 4 * 4 * 128 * 128 * 4         # 4 groups x 1 tile x 4 slices
     assert call(sched=s) == _lib.E_WORKSPACE
     assert call(sched=S(tile=(96, 96))) == _lib.E_UNSUPPORTED
     n = ctypes.c_int64(-1)
