@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "BST_OK", -1: "BST_E_INVAL", -2: "BST_E_UNSUPPORTED", -3: "BS
 # bst_dtype
 F16, BF16, E4M3, MXE4M3, I8, I32, F32 = 1, 2, 3, 4, 5, 6, 7
 
-EXPORTS = ["bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
+EXPORTS = ["bst_gemm", "bst_gemm_noalloc", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
            "bst_grouped_gemm_slice_m", "bst_grouped_gemm_slice_k", "bst_quant_gemm_per_token",
            "bst_tile_map", "bst_grouped_tile_map", "bst_workspace_bytes", "bst_effective_sched",
            "bst_task_count", "bst_last_error", "bst_version"]
@@ -52,6 +52,8 @@ def lib():
             i64, i32, p, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
             sz, sp = ctypes.c_size_t, ctypes.POINTER(Sched)
             L.bst_gemm.argtypes = [st, st, i64, i64, i64, p, i64, p, i64, p, i64, p, p, sp, p, sz, p]
+            L.bst_gemm_noalloc.argtypes = [st, st, i64, i64, i64, p, i64, p, i64, p, i64, p, p,
+                                           sp, p]
             L.bst_gemm_add.argtypes = [st, st, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, p,
                                        sp, p, sz, p]
             L.bst_gemm_padded.argtypes = [st, st, i64, i64, i64, p, i64, p, i64, p, i64, p, p, sp,
@@ -71,7 +73,7 @@ def lib():
             L.bst_effective_sched.argtypes = [ctypes.c_int, st, i64, i64, i64, i64, sp, sp]
             L.bst_task_count.argtypes = [ctypes.c_int, st, i64, i64, i64, sp,
                                          ctypes.POINTER(i64)]
-            for fn in ("bst_gemm", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
+            for fn in ("bst_gemm", "bst_gemm_noalloc", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
                        "bst_grouped_gemm_slice_m", "bst_grouped_gemm_slice_k",
                        "bst_quant_gemm_per_token", "bst_tile_map", "bst_grouped_tile_map",
                        "bst_effective_sched", "bst_task_count"):

@@ -479,6 +479,50 @@ bst_status repack(bst_dtype ab, const void* src, int64_t sld, void* dst, int64_t
   return BST_OK;
 }
 
+// ------------------------------------------------- static scratch -------
+// The scratch of bst_gemm_noalloc: a workspace (counter area, then split-K
+// partials) that lives in the library's own device memory, one copy per GPU
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not the device address: the address comes from
+// hipGetSymbolAddress, once per device (scratch_ptr), and only that address
+// is passed to kernels.
+constexpr size_t kScratchBytes = 32u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch;  // device -> address of its scratch
+
+__global__ void zero_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The current device's scratch address; on the first call for a device, its
+// counter area is cleared on `stream` (a fill kernel, so that a capturing
+// caller records no memset node).
+bst_status scratch_ptr(void* stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BST_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return BST_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(BST_E_HIP, "hipGetSymbolAddress of the scratch failed: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<uint32_t*>(ptr), (uint32_t)(kCounterBytes / 4));
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(BST_E_HIP, "scratch clear failed: %s", hipGetErrorString(e));
+  g_scratch[dev] = ptr;
+  *out = ptr;
+  return BST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -499,6 +543,36 @@ bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K, 
     return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
   return dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
                nullptr, s, ws, ws_bytes, stream);
+}
+
+bst_status bst_gemm_noalloc(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                            int64_t ldc, const uint8_t* scale_a, const uint8_t* scale_b,
+                            const bst_sched* s, void* stream) {
+  if (ab != BST_MXE4M3 && (scale_a || scale_b))
+    return fail(BST_E_INVAL, "block scales are only taken with BST_MXE4M3");
+  // every check first, against a stand-in address of the scratch's size
+  Plan p;
+  GemmArgs a{};
+  bool empty = true;
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t{256});
+  bst_status st = make_plan(FORM_DENSE, ab, 1, M, N, K, s, false, p);
+  if (st != BST_OK) return st;
+  if (p.ws_bytes > kScratchBytes)
+    return fail(BST_E_WORKSPACE, "this schedule needs %zu workspace bytes; the static scratch of "
+                "bst_gemm_noalloc holds %zu (use a smaller split_k, or bst_gemm with a workspace)",
+                p.ws_bytes, kScratchBytes);
+  st = prepare_dense(ab, c, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, scale_a, scale_b, nullptr,
+                     nullptr, s, stand_in, kScratchBytes, nullptr, 0, p, a, empty);
+  if (st != BST_OK || empty) return st;
+  if (p.ws_bytes > kScratchBytes)  // the plan made with the device's CU count
+    return fail(BST_E_WORKSPACE, "this schedule needs %zu workspace bytes; the static scratch of "
+                "bst_gemm_noalloc holds %zu", p.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_ptr(stream, &ws);
+  if (st != BST_OK) return st;
+  fill_ws(a, p, ws);
+  return launch(p, a, stream);
 }
 
 bst_status bst_gemm_add(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K, const void* A,

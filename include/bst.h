@@ -135,6 +135,27 @@ bst_status bst_gemm(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
                     size_t ws_bytes, void* stream);
 
 /*
+ * bst_gemm_noalloc -- bst_gemm for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operands, schedule and results, and no workspace
+ * argument.  The split-K partials and counters and the dynamic-allocation
+ * queues live in a static scratch array inside the library: 32 MiB of
+ * device memory per GPU, held from the library's load until the process
+ * ends, addressed once per device (hipGetSymbolAddress) on the first call
+ * there, which also clears its counter area on `stream`.  The call itself
+ * allocates and frees nothing.  A schedule needing more than 32 MiB
+ * (bst_workspace_bytes) returns BST_E_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's scratch and leaves its
+ * counters zero again when it completes: calls that overlap on one GPU
+ * (different streams, or host threads without ordering) race and must not
+ * be issued.
+ */
+bst_status bst_gemm_noalloc(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int64_t K,
+                            const void* A_dev, int64_t lda, const void* B_dev, int64_t ldb,
+                            void* C_dev, int64_t ldc, const uint8_t* scale_a_dev,
+                            const uint8_t* scale_b_dev, const bst_sched* sched, void* stream);
+
+/*
  * bst_gemm_add -- C = A . B + X (the matmul-add example that "Block Dispatch
  * Policies" lists under its ping-pong policy; reading: X has C's shape and
  * dtype c).  Same operands, scales, schedule and workspace as bst_gemm.
