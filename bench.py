@@ -17,6 +17,8 @@ of MI355X (2.5 PFLOP/s; 5.0 for fp8); `cpu_baseline` times the CPU oracle
 
 Other modes (one JSON line per measurement): --all-configs (every workload
 configuration), --l2-sweep (every swizzle setting, for rocprofv3 counters),
+--sweep-configs (every configuration's schedules, for rocprofv3 counters),
+--summarize (the table of a sweep's rocprofv3 runs),
 --large (4096^3 and 8192x8192x4096 beside the library GEMMs torch calls),
 --clock (shader clock under each workload, with the cycle-accounting build),
 --calib-copy and --traffic-from (HBM traffic calibration and summary).
@@ -122,9 +124,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     p.add_argument("--l2-sweep", action="store_true",
-                   help="only run the fp16 workload under every swizzle setting (Zn / Nz offsets "
-                        "1, 2, 4, 8 and RASTER, XCD remap off / on) at the 256x128 and the 64x64 "
-                        "tile, --steps launches each, for per-setting rocprofv3 counters")
+                   help="only run the fp16 and MX-fp8 workloads under every swizzle setting (Zn / "
+                        "Nz offsets 1, 2, 4, 8 and RASTER, XCD remap off / on) at their named and "
+                        "fastest tiles, --steps launches each, for per-setting rocprofv3 counters")
     p.add_argument("--all-configs", action="store_true",
                    help="time every workload configuration (one JSON line per schedule)")
     p.add_argument("--traffic-from", default="",
@@ -135,6 +137,17 @@ def parse():
     p.add_argument("--clock", action="store_true",
                    help="with the cycle-accounting build (python -m block_swizzle_tile_amd.build "
                         "--trace): the shader clock each workload's workgroups ran at")
+    p.add_argument("--phases", action="store_true",
+                   help="with the cycle-accounting build (python -m block_swizzle_tile_amd.build "
+                        "--trace): where a work unit's cycles go, per workload")
+    p.add_argument("--sweep-configs", action="store_true",
+                   help="launch every configuration's named and fastest schedules --steps times "
+                        "each, eagerly and in a fixed order, for per-dispatch rocprofv3 counters")
+    p.add_argument("--plan-out", default="",
+                   help="with --l2-sweep / --sweep-configs: write the launch plan here")
+    p.add_argument("--summarize", default="",
+                   help="print the per-setting table of the rocprofv3 runs of a sweep under this "
+                        "folder (plan.json, trace/, tcc/, fetch/, write/, sq/, calib_*/)")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run plain 256 MiB device copies (the known-size reference that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -173,36 +186,314 @@ def time_launches(fn, steps, warmup, min_warm_s=0.1):
     return total, total / steps
 
 
+def median_launch(bst, fn, n=50):
+    """Median over n launches of fn() of each launch's span on the device: from its first
+    workgroup's start to its last workgroup's end, read from the production kernels'
+    clock record (100 MHz reference counter, 10 ns steps).  Launches run eagerly one after
+    another; the span leaves out the host's launch overhead and the dispatch before the
+    first workgroup starts.  Returns ms (after at least 0.1 s of warm-up launches)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        fn()
+        torch.cuda.synchronize()
+    nwg = 1024
+    buf = torch.zeros((n, nwg, 4), dtype=torch.int64, device="cuda")
+    try:
+        for i in range(n):
+            bst.clock_record(buf[i], nwg)
+            fn()
+    finally:
+        bst.clock_record()
+    torch.cuda.synchronize()
+    t = buf.cpu()
+    spans = []
+    for i in range(n):
+        r = t[i][t[i][:, 3] == 1]
+        spans.append(float(r[:, 1].max() - r[:, 0].min()) / 100.0 / 1e3)   # ms
+    spans.sort()
+    return spans[len(spans) // 2]
+
+
+def shader_clock(bst, fn):
+    """Shader clock (MHz) the workgroups of one launch of fn() ran at, from the production
+    kernels' clock record (bst_set_clock_record): median, min and max over the recorded
+    workgroups, after at least 0.1 s of warm-up launches."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        fn()
+        torch.cuda.synchronize()
+    buf = torch.zeros(4 * 1024, dtype=torch.int64, device="cuda")
+    bst.clock_record(buf, 1024)
+    try:
+        fn()
+        torch.cuda.synchronize()
+    finally:
+        bst.clock_record()
+    t = buf.cpu().view(1024, 4)
+    t = t[t[:, 3] == 1].double()
+    ticks = (t[:, 1] - t[:, 0]).clamp(min=1)
+    mhz = t[:, 2] / (ticks / 100.0)
+    return {"sclk_mhz_median": round(float(mhz.median()), 0),
+            "sclk_mhz_min": round(float(mhz.min()), 0),
+            "sclk_mhz_max": round(float(mhz.max()), 0), "workgroups": int(t.shape[0])}
+
+
+def _run_plan(args, plan, runners, torch):
+    """Launch every planned setting args.steps times (eager, in plan order), after writing the
+    plan (label, workload, schedule, flop and MFMA cycles per launch) to args.plan_out, so a
+    rocprofv3 run can attribute its per-dispatch records to settings."""
+    bst = sys.modules["block_swizzle_tile_amd"]
+    print(json.dumps({"plan": plan, "launches_each": args.steps}), flush=True)
+    if args.plan_out:
+        with open(args.plan_out, "w") as f:
+            json.dump({"plan": plan, "launches_each": args.steps}, f, indent=1)
+    for c in plan:
+        kw = dict(c["sched"])
+        kw["tile"] = tuple(kw["tile"])
+        s = bst.make_sched(**kw)
+        for _ in range(args.steps):
+            runners[c["workload"]](s)
+        torch.cuda.synchronize()
+
+
+# flop per MFMA cycle of one SIMD, per operand type: 32x32x16 f16 / bf16 every 32 cycles, i8
+# 32x32x32 every 32, scaled f8f6f4 32x32x64 every 64
+MFMA_FLOP_PER_CLK = {"f16": 1024, "bf16": 1024, "i8": 2048, "e4m3": 2048}
+
+
 def l2_sweep(args, bst, I, gpu, torch):
-    """Every swizzle setting on the fp16 1024x1024x2048 workload, in a fixed
-    order printed first as JSON (one kernel launch per step, no graph), so a
-    rocprofv3 run can attribute its per-dispatch counters to settings."""
+    """Every swizzle setting on the fp16 1024x1024x2048 workload (tiles 256x128 and 64x64)
+    and on the MX-fp8 1024x2048x4096 one (256x256 and 64x128): Zn / Nz with offsets 1, 2,
+    4, 8 and RASTER, each with the XCD remap off and on, split 1."""
     w = I.workload("fp16_2k")
     A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
     C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
-    cfgs = []
-    for tile in ((256, 128), (64, 64)):
-        for remap in (0, 1):
-            for d in ("zn", "nz"):
-                for off in (1, 2, 4, 8):
-                    cfgs.append({"tile": tile, "direction": d, "offset": off, "xcd_remap": remap})
-            cfgs.append({"tile": tile, "direction": "raster", "offset": 1, "xcd_remap": remap})
-    print(json.dumps({"l2_sweep": cfgs, "launches_each": args.steps}), flush=True)
-    for c in cfgs:
-        s = bst.make_sched(tile=c["tile"], offset=c["offset"], direction=c["direction"],
-                           split_k=1, xcd_remap=c["xcd_remap"])
-        for _ in range(args.steps):
-            bst.gemm(A, B, C, sched=s)
-        torch.cuda.synchronize()
+    x = I.workload("mxfp8_4k")
+    Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
+    sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
+    Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
+    runners = {"fp16_2k": lambda s: bst.gemm(A, B, C, sched=s),
+               "mxfp8_4k": lambda s: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s)}
+    f2, f3 = 2.0 * 1024 * 1024 * 2048, 2.0 * 1024 * 2048 * 4096
+    plan = []
+    for wl, dt, flop, tiles in (("fp16_2k", "f16", f2, ((256, 128), (64, 64))),
+                                ("mxfp8_4k", "e4m3", f3, ((256, 256), (64, 128)))):
+        for tile in tiles:
+            for remap in (0, 1):
+                orders = [(d, off) for d in ("zn", "nz") for off in (1, 2, 4, 8)] + [("raster", 1)]
+                for d, off in orders:
+                    label = "%s %dx%d remap%d %s" % (wl, tile[0], tile[1], remap,
+                                                     "RASTER" if d == "raster" else "%s%d" % (d.capitalize(), off))
+                    plan.append({"label": label, "workload": wl, "dtype": dt, "flop": flop,
+                                 "mfma_cycles": flop / MFMA_FLOP_PER_CLK[dt],
+                                 "alg_bytes": 10485760 if wl == "fp16_2k" else 17170432,
+                                 "sched": {"tile": list(tile), "offset": off, "direction": d,
+                                           "xcd_remap": remap}})
+    _run_plan(args, plan, runners, torch)
+
+
+def sweep_configs(args, bst, I, gpu, torch):
+    """Each workload configuration at its named tile and at its fastest schedules (the
+    --all-configs set, padding matmul aside), for per-dispatch rocprofv3 counters."""
+    w = I.workload("tails")
+    A1, B1 = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C1 = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    w = I.workload("fp16_2k")
+    A2, B2 = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C2 = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    x = I.workload("mxfp8_4k")
+    Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
+    sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
+    Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
+    b = I.workload("bf16_batch")
+    Ab, Bb = gpu(b["A"], "bf16"), gpu(b["B"], "bf16")
+    Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
+    g = I.workload("int8_groups")
+    Ag, Bg, gm = gpu(g["A"], "i8"), gpu(g["B"], "i8"), gpu(g["group_m"], "i32")
+    rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
+    Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
+    k = I.workload("int8_slice_k")
+    Ak, Bk, gk = gpu(k["A"], "i8"), gpu(k["B"], "i8"), gpu(k["group_k"], "i32")
+    rk, ck = gpu(k["row_scale"], "f32"), gpu(k["col_scale"], "f32")
+    Ck = torch.empty((k["G"], k["M"], k["N"]), dtype=torch.bfloat16, device="cuda")
+    runners = {
+        "C1": lambda s: bst.gemm(A1, B1, C1, sched=s),
+        "C2": lambda s: bst.gemm(A2, B2, C2, sched=s),
+        "C3": lambda s: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s),
+        "C4": lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s),
+        "C5": lambda s: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs,
+                                                 sched=s),
+        "SK": lambda s: bst.grouped_gemm_slice_k(Ak, Bk, gk, Ck, row_scale=rk, col_scale=ck,
+                                                 sched=s),
+    }
+    info = {  # workload: (name, dtype, flop, algorithmic bytes)
+        "C1": ("C1 fp16 200x136x256", "f16", 2.0 * 200 * 136 * 256, 226432),
+        "C2": ("C2 fp16 1024x1024x2048", "f16", 2.0 * 1024 * 1024 * 2048, 10485760),
+        "C3": ("C3 MX-fp8 1024x2048x4096", "e4m3", 2.0 * 1024 * 2048 * 4096, 17170432),
+        "C4": ("C4 bf16 16x512x768x1024", "bf16", 2.0 * 16 * 512 * 768 * 1024, 54525952),
+        "C5": ("C5 int8 grouped 8192x4096x2048 dequant", "i8", 2.0 * 8192 * 4096 * 2048,
+               151158816),
+        "SK": ("int8 slice-K 8x(1024x2048) K 8192 dequant", "i8", 2.0 * 1024 * 2048 * 8192,
+               1024 * 8192 + 8192 * 2048 + 8 * 1024 * 2048 * 2 + 8 * (1024 + 2048) * 4),
+    }
+    scheds = [
+        ("C1", dict(tile=[64, 64], offset=3, direction="zn")),
+        ("C2", dict(tile=[256, 128], offset=4, direction="zn")),
+        ("C2", dict(tile=[64, 64], offset=8, direction="zn", xcd_remap=1, shuffle_k=1)),
+        ("C3", dict(tile=[256, 256], offset=4, direction="zn")),
+        ("C3", dict(tile=[64, 128], offset=8, direction="zn", xcd_remap=1)),
+        ("C4", dict(tile=[128, 192], offset=1, direction="zn")),
+        ("C4", dict(tile=[128, 192], offset=1, direction="zn", xcd_remap=1)),
+        ("C5", dict(tile=[256, 256], offset=1, direction="zn")),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1)),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, dynamic=1)),
+        ("SK", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1)),
+    ]
+    plan = []
+    for wl, kw in scheds:
+        name, dt, flop, alg = info[wl]
+        label = "%s %dx%d %s%s" % (name, kw["tile"][0], kw["tile"][1],
+                                   "%s%d" % (kw["direction"].capitalize(), kw["offset"]),
+                                   "".join(" %s" % k for k in ("xcd_remap", "shuffle_k", "dynamic")
+                                           if kw.get(k)))
+        plan.append({"label": label, "workload": wl, "dtype": dt, "flop": flop,
+                     "mfma_cycles": flop / MFMA_FLOP_PER_CLK[dt], "alg_bytes": alg, "sched": kw})
+    _run_plan(args, plan, runners, torch)
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _ours(name):
+    return "bst::gemm" in name
+
+
+def summarize(d):
+    """Markdown table of a sweep's rocprofv3 runs under d: plan.json (from --plan-out),
+    trace/ (--kernel-trace), tcc/ (TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum), fetch/
+    (FETCH_SIZE), write/ (WRITE_SIZE), sq/ (SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT
+    SQ_INSTS_LDS) and, for the copy calibration, calib_fetch/ and calib_write/ (FETCH_SIZE /
+    WRITE_SIZE of --calib-copy).  Per setting, medians over its launches after the first."""
+    plan = json.load(open(os.path.join(d, "plan.json")))
+    n, settings = plan["launches_each"], plan["plan"]
+
+    def per_dispatch(sub, counter):
+        rows = [r for r in _csv_rows(os.path.join(d, sub), "counter_collection.csv")
+                if r["Counter_Name"] == counter and _ours(r["Kernel_Name"])]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [float(r["Counter_Value"]) for r in rows]
+
+    def med(v):
+        v = sorted(v[1:] if len(v) > 2 else v)   # the first launch of a setting is cold
+        return v[len(v) // 2] if v else float("nan")
+
+    def chunks(vals):
+        if len(vals) != n * len(settings):
+            return None
+        return [vals[i * n:(i + 1) * n] for i in range(len(settings))]
+
+    tr = [r for r in _csv_rows(os.path.join(d, "trace"), "kernel_trace.csv") if _ours(r["Kernel_Name"])]
+    tr.sort(key=lambda r: int(r["Dispatch_Id"]))
+    dur = chunks([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in tr])
+    hit, miss, rdreq = (chunks(per_dispatch("tcc", c)) for c in ("TCC_HIT_sum", "TCC_MISS_sum",
+                                                                "TCC_EA0_RDREQ_sum"))
+    fetch, write = chunks(per_dispatch("fetch", "FETCH_SIZE")), chunks(per_dispatch("write", "WRITE_SIZE"))
+    mfma, conf = (chunks(per_dispatch("sq", c)) for c in ("SQ_VALU_MFMA_BUSY_CYCLES",
+                                                        "SQ_LDS_BANK_CONFLICT"))
+    cal = 256 << 20
+    cf = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(d, "calib_fetch"), "counter_collection.csv")
+          if r["Counter_Name"] == "FETCH_SIZE" and "copy" in r["Kernel_Name"].lower()]
+    cw = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(d, "calib_write"), "counter_collection.csv")
+          if r["Counter_Name"] == "WRITE_SIZE" and "copy" in r["Kernel_Name"].lower()]
+    sf = cal / (med(cf) * 1024.0) if cf else float("nan")
+    sw = cal / (med(cw) * 1024.0) if cw else float("nan")
+    print("Copy calibration: FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (bytes per KiB counted "
+          "/ 1024)\n" % (sf, sw))
+    print("| setting | median us | TFLOP/s | L2 hit % | fabric rd req (x1000) | HBM MB "
+          "(alg MB) | HBM GB/s | MFMA busy / needed | LDS conflicts |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for i, c in enumerate(settings):
+        us = med(dur[i]) if dur else float("nan")
+        h = med(hit[i]) if hit else float("nan")
+        m = med(miss[i]) if miss else float("nan")
+        hb = (med(fetch[i]) * 1024 * sf + med(write[i]) * 1024 * sw) if (fetch and write) else float("nan")
+        print("| %s | %.2f | %.1f | %.1f | %.0f | %.1f (%.1f) | %.0f | %s | %s |" % (
+            c["label"], us, c["flop"] / (us * 1e-6) / 1e12, 100.0 * h / (h + m),
+            (med(rdreq[i]) / 1000.0) if rdreq else float("nan"), hb / 1e6, c["alg_bytes"] / 1e6,
+            hb / (us * 1e-6) / 1e9,
+            ("%.3f" % (med(mfma[i]) / c["mfma_cycles"])) if mfma else "-",
+            ("%.0f" % med(conf[i])) if conf else "-"))
+
+
+def cold_launch(torch, fn, n=20, scrub_bytes=512 << 20):
+    """Median ms of n launches of fn(), each timed alone right after a 512 MiB scrub write
+    (a fill kernel over a buffer twice the size of the MALL), so that its operands come
+    from HBM rather than the caches."""
+    scrub = torch.empty(scrub_bytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+    ms = []
+    fn()
+    for i in range(n):
+        scrub.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del scrub
+    ms.sort()
+    return ms[len(ms) // 2]
+
+
+def oracle_time(orc, name, flop_per_row, nrows_total, run_rows, threads=0, budget_s=6.0):
+    """The oracle on whole output rows of one workload: the largest sample of evenly spread
+    rows (doubling from 1) whose pass takes under budget_s, timed once; returns a
+    cpu_baseline-style record in TFLOP/s (threads: 0 = the oracle's default)."""
+    import numpy as np
+    prev = orc.threads()
+    used = orc.threads(threads) if threads > 0 else prev
+    try:
+        n = 1
+        while True:
+            rows = np.linspace(0, nrows_total - 1, min(n, nrows_total)).astype(np.int64)
+            t0 = time.perf_counter()
+            run_rows(rows)
+            dt = time.perf_counter() - t0
+            if dt * 2.2 > budget_s or n >= nrows_total:
+                break
+            n *= 2
+    finally:
+        orc.threads(prev)
+    rec = {"config": name, "cpu_baseline": {
+        "value": round(flop_per_row * len(rows) / dt / 1e12, 6), "unit": "TFLOP/s",
+        "cores": used, "kind": "oracle",
+        "sample": "%d of %d output rows (fp64 / int64 oracle, %.2f s)" % (len(rows), nrows_total, dt)}}
+    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def all_configs(args, bst, I, gpu, torch):
     """Every configuration of the workload set, at its stated tile and at the
     faster schedules, timed like the headline (warm, graph replay of
-    args.steps launches); one JSON line per (config, schedule)."""
+    args.steps launches); one JSON line per (config, schedule).  Each
+    configuration's fastest schedule also gets its shader clock; C4 and C5
+    (whose operands exceed the L2s) also a cold figure; and the oracle is
+    timed on a sample of each configuration's rows on this host (C1 and C2
+    also on one thread)."""
+    import numpy as np
+    import oracle as orc
     out = []
 
-    def run(name, flop, dtype, sched_kw, fn):
+    def run(name, flop, dtype, sched_kw, fn, cold=False, clock=False):
         s = bst.make_sched(**sched_kw)
         tot, per = time_launches(lambda: fn(s), args.steps, args.warmup)
         tf = flop / (per * 1e-3) / 1e12
@@ -210,6 +501,15 @@ def all_configs(args, bst, I, gpu, torch):
                                          for k, v in sched_kw.items()},
                "us_per_launch": round(per * 1e3, 3), "tflops": round(tf, 2),
                "pct_of_peak": round(100.0 * tf / PEAK[dtype], 2)}
+        if cold:
+            cms = cold_launch(torch, lambda: fn(s))
+            rec["cold_us"] = round(cms * 1e3, 3)
+            rec["cold_tflops"] = round(flop / (cms * 1e-3) / 1e12, 2)
+        if clock:
+            clk = shader_clock(bst, lambda: fn(s))
+            rec["sclk_mhz"] = clk["sclk_mhz_median"]
+            rec["pct_at_measured_clock"] = round(
+                100.0 * tf / (PEAK[dtype] * clk["sclk_mhz_median"] / 2400.0), 2)
         out.append(rec)
         print(json.dumps(rec), flush=True)
 
@@ -218,7 +518,12 @@ def all_configs(args, bst, I, gpu, torch):
     C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
     f1 = 2.0 * w["M"] * w["N"] * w["K"]
     run("C1 fp16 200x136x256", f1, "f16", dict(tile=(64, 64), offset=3, direction="zn"),
-        lambda s: bst.gemm(A, B, C, sched=s))
+        lambda s: bst.gemm(A, B, C, sched=s), clock=True)
+    for thr in (0, 1):
+        oracle_time(orc, "C1 fp16 200x136x256" + (" (1 thread)" if thr else ""),
+                    2.0 * w["N"] * w["K"], w["M"],
+                    lambda rows: orc.gemm(orc.F16, w["A"], w["B"], tile=(64, 64), off=3,
+                                          rows=rows), threads=thr)
 
     w = I.workload("fp16_2k")
     A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
@@ -226,9 +531,16 @@ def all_configs(args, bst, I, gpu, torch):
     f2 = 2.0 * w["M"] * w["N"] * w["K"]
     for kw in (dict(tile=(256, 128), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(256, 128), offset=4, direction="zn", xcd_remap=0),
-               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1),
-               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1)):
+               dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1)):
         run("C2 fp16 1024x1024x2048", f2, "f16", kw, lambda s: bst.gemm(A, B, C, sched=s))
+    run("C2 fp16 1024x1024x2048", f2, "f16",
+        dict(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1),
+        lambda s: bst.gemm(A, B, C, sched=s), clock=True)
+    for thr in (0, 1):
+        oracle_time(orc, "C2 fp16 1024x1024x2048" + (" (1 thread)" if thr else ""),
+                    2.0 * w["N"] * w["K"], w["M"],
+                    lambda rows: orc.gemm(orc.F16, w["A"], w["B"], tile=(64, 64), rows=rows),
+                    threads=thr)
 
     # matmul-add on the same workload: C = A.B + X with a seeded fp16 addend
     X = gpu(I.uniform_f16((w["M"], w["N"]), I.WORKLOAD_IDS["fp16_2k"], 7, -4.0, 4.0), "f16")
@@ -253,20 +565,31 @@ def all_configs(args, bst, I, gpu, torch):
     Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
     f3 = 2.0 * x["M"] * x["N"] * x["K"]
     for kw in (dict(tile=(256, 256), offset=4, direction="zn", xcd_remap=0),
-               dict(tile=(256, 256), offset=4, direction="zn", xcd_remap=1),
-               dict(tile=(64, 128), offset=8, direction="zn", xcd_remap=1)):
+               dict(tile=(256, 256), offset=4, direction="zn", xcd_remap=1)):
         run("C3 MX-fp8 1024x2048x4096", f3, "e4m3", kw,
             lambda s: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s))
+    run("C3 MX-fp8 1024x2048x4096", f3, "e4m3", dict(tile=(64, 128), offset=8, direction="zn",
+                                                     xcd_remap=1),
+        lambda s: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=s), clock=True)
+    oracle_time(orc, "C3 MX-fp8 1024x2048x4096", 2.0 * x["N"] * x["K"], x["M"],
+                lambda rows: orc.gemm(orc.MXE4M3, x["A"], x["B"], scale_a=x["scale_a"],
+                                      scale_b=x["scale_b"], tile=(256, 256), off=4, rows=rows))
 
     b = I.workload("bf16_batch")
     Ab, Bb = gpu(b["A"], "bf16"), gpu(b["B"], "bf16")
     Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
     f4 = 2.0 * b["batch"] * b["M"] * b["N"] * b["K"]
     for kw in (dict(tile=(128, 192), offset=1, direction="zn"),
-               dict(tile=(128, 192), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1),
                dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1)):
         run("C4 bf16 16x512x768x1024", f4, "bf16", kw, lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s))
+    run("C4 bf16 16x512x768x1024", f4, "bf16", dict(tile=(128, 192), offset=1, direction="zn",
+                                                    xcd_remap=1),
+        lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s), cold=True, clock=True)
+    oracle_time(orc, "C4 bf16 16x512x768x1024", 2.0 * b["N"] * b["K"], b["batch"] * b["M"],
+                lambda rows: orc.gemm(orc.BF16, b["A"], b["B"], batch=b["batch"], M=b["M"],
+                                      N=b["N"], K=b["K"], strideA=b["M"] * b["K"],
+                                      strideB=b["K"] * b["N"], tile=(128, 192), rows=rows))
 
     g = I.workload("int8_groups")
     Ag, Bg = gpu(g["A"], "i8"), gpu(g["B"], "i8")
@@ -274,13 +597,38 @@ def all_configs(args, bst, I, gpu, torch):
     rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
     Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
     f5 = 2.0 * g["total_m"] * g["N"] * g["K"]
+    c5 = lambda s: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs, sched=s)
     for kw in (dict(tile=(256, 256), offset=1, direction="zn"),
                dict(tile=(256, 256), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, preload=1)):
+        run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8", kw, c5)
+    run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8",
+        dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, dynamic=1), c5,
+        cold=True, clock=True)
+    oracle_time(orc, "C5 int8 grouped 8192x4096x2048 dequant", 2.0 * g["N"] * g["K"],
+                int(g["group_m"].sum()),
+                lambda rows: orc.grouped_gemm(g["group_m"], g["A"], g["B"], g["N"], g["K"],
+                                              row_scale=g["row_scale"], col_scale=g["col_scale"],
+                                              tile=(128, 128), off=4, rows=rows))
+
+    k = I.workload("int8_slice_k")
+    Ak, Bk, gk = gpu(k["A"], "i8"), gpu(k["B"], "i8"), gpu(k["group_k"], "i32")
+    rk, ck = gpu(k["row_scale"], "f32"), gpu(k["col_scale"], "f32")
+    Ck = torch.empty((k["G"], k["M"], k["N"]), dtype=torch.bfloat16, device="cuda")
+    fk = 2.0 * k["M"] * k["N"] * k["total_k"]
+    for kw in (dict(tile=(256, 256), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)):
-        run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8", kw,
-            lambda s: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs,
-                                                sched=s))
+        run("int8 grouped slice-K 8 x (1024x2048), K 8192, dequant", fk, "i8", kw,
+            lambda s: bst.grouped_gemm_slice_k(Ak, Bk, gk, Ck, row_scale=rk, col_scale=ck, sched=s),
+            clock=kw["tile"] == (128, 128))
+    oracle_time(orc, "int8 grouped slice-K 8 x (1024x2048), K 8192, dequant",
+                2.0 * k["N"] * k["total_k"] / k["G"], k["G"] * k["M"],
+                lambda rows: orc.grouped_gemm_slice_k(orc.I8, k["group_k"], k["A"], k["B"],
+                                                      k["M"], k["N"], row_scale=k["row_scale"],
+                                                      col_scale=k["col_scale"], tile=(128, 128),
+                                                      rows=rows))
     return out
 
 
@@ -420,6 +768,87 @@ def clock(args, torch, np, I, gpu):
         del A, B, C, kw
 
 
+def phases(args, torch, np, I, gpu):
+    """Where a work unit's shader cycles go, from the cycle-accounting build (python -m
+    block_swizzle_tile_amd.build --trace): workgroup 0's waves record, per unit, the set-up
+    (decode, lane offsets; the first unit from the kernel's start), the K loop (its prologue,
+    the waits at the stage barriers and the step bodies), the split-K fix-up and the
+    epilogue (stores issued, then complete).  Averages over the waves and the units of 5
+    launches (after 20 untimed ones), one JSON line per workload.  The build runs about 20%
+    slower than the production one; the split between phases is what it is for."""
+    import ctypes
+    from block_swizzle_tile_amd import _lib as L
+    from block_swizzle_tile_amd import build as bld
+    if not os.path.exists(bld.TRACE_LIB):
+        sys.exit("bench.py --phases needs %s (python -m block_swizzle_tile_amd.build --trace)"
+                 % bld.TRACE_LIB)
+    L.LIB_PATH = bld.TRACE_LIB
+    import block_swizzle_tile_amd as bst
+    lib = L.lib()
+    lib.bst_debug_set_trace.argtypes = [ctypes.c_void_p]
+    lib.bst_debug_set_trace.restype = None
+    tr = torch.zeros(128 + 4 * 256, dtype=torch.int64, device="cuda")
+
+    def one(name, fn, waves=4):
+        lib.bst_debug_set_trace(None)
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        tr.zero_()
+        lib.bst_debug_set_trace(ctypes.c_void_p(tr.data_ptr()))
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        lib.bst_debug_set_trace(None)
+        t = tr.cpu().numpy().astype(np.float64)
+        loop = t[:32].reshape(8, 4)[:waves]       # wait, body, prologue, total
+        task = t[32:64].reshape(8, 4)[:waves]     # set-up, K loop, fix-up + epilogue, units
+        epi = t[64:96].reshape(8, 4)[:waves]      # fix-up, stores issued, stores complete
+        units = task[:, 3].mean()
+        per = lambda v: round(float(v.mean() / units), 0)
+        print(json.dumps({"workload": name, "units_per_launch_wg0": round(units / 5, 2),
+                          "setup": per(task[:, 0]), "k_loop": per(task[:, 1]),
+                          "k_loop_prologue": per(loop[:, 2]), "k_loop_waits": per(loop[:, 0]),
+                          "k_loop_bodies": per(loop[:, 1]), "fixup": per(epi[:, 0]),
+                          "stores_issued": per(epi[:, 1]), "stores_complete": per(epi[:, 2]),
+                          "unit": "shader cycles per work unit (workgroup 0, wave mean)"}),
+              flush=True)
+
+    w = I.workload("fp16_2k")
+    A, B = gpu(w["A"], "f16"), gpu(w["B"], "f16")
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    s = bst.make_sched(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1)
+    one("C2 fp16 1024x1024x2048 64x64", lambda: bst.gemm(A, B, C, sched=s))
+    x = I.workload("mxfp8_4k")
+    Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
+    sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")
+    Cx = torch.empty((x["M"], x["N"]), dtype=torch.bfloat16, device="cuda")
+    sx = bst.make_sched(tile=(64, 128), offset=8, direction="zn", xcd_remap=1)
+    one("C3 MX-fp8 1024x2048x4096 64x128", lambda: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb,
+                                                            sched=sx))
+    b = I.workload("bf16_batch")
+    Ab, Bb = gpu(b["A"], "bf16"), gpu(b["B"], "bf16")
+    Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
+    sbt = bst.make_sched(tile=(128, 192), offset=1, direction="zn", xcd_remap=1)
+    one("C4 bf16 16x512x768x1024 128x192", lambda: bst.batched_gemm(Ab, Bb, Cb, sched=sbt))
+    g = I.workload("int8_groups")
+    Ag, Bg, gm = gpu(g["A"], "i8"), gpu(g["B"], "i8"), gpu(g["group_m"], "i32")
+    rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
+    Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
+    for extra in ({}, {"preload": 1}, {"dynamic": 1}):
+        sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, **extra)
+        one("C5 int8 grouped 128x128 %s" % (" ".join(extra) or "static"),
+            lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs, sched=sg))
+    sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)
+    Craw = torch.empty((g["total_m"], g["N"]), dtype=torch.int32, device="cuda")
+    one("C5 int8 grouped 128x128 raw int32 (no dequant)",
+        lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Craw, sched=sg))
+    for i, (wl, M, N, K) in enumerate(LARGE_SHAPES[1:2]):
+        Al, Bl, Cl, kw = large_operands(torch, wl, M, N, K, 1001)
+        sl = bst.make_sched(tile=(256, 256), offset=4, direction="zn", xcd_remap=1)
+        one("fp16 8192x8192x4096 256x256", lambda: bst.gemm(Al, Bl, Cl, sched=sl, **kw), waves=8)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -429,6 +858,9 @@ def main():
         sys.exit(2)
     if args.traffic_from:
         traffic_summary(args.traffic_from, CALIB_BYTES)
+        return
+    if args.summarize:
+        summarize(args.summarize)
         return
     import numpy as np
     import torch
@@ -458,6 +890,9 @@ def main():
     if args.clock:
         clock(args, torch, np, I, gpu)
         return
+    if args.phases:
+        phases(args, torch, np, I, gpu)
+        return
     import block_swizzle_tile_amd as bst
     if args.large:
         large(args, bst, torch)
@@ -467,6 +902,9 @@ def main():
         return
     if args.l2_sweep:
         l2_sweep(args, bst, I, gpu, torch)
+        return
+    if args.sweep_configs:
+        sweep_configs(args, bst, I, gpu, torch)
         return
 
     # ---------------------------------------------------------- fp16 2k --
@@ -491,6 +929,12 @@ def main():
     value = flop * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flop / (mean_ms * 1e-3) / 1e12
 
+    # the same launch timed alone (median of 50), the shader clock it runs at, and the tile
+    # the workload's definition names (256 x 128, SwizzleOffset 4, Zn)
+    med_ms = median_launch(bst, step)
+    clk = shader_clock(bst, step)
+    named = bst.make_sched(tile=(256, 128), offset=4, direction="zn")
+    named_per = time_launches(lambda: bst.gemm(A, B, C, sched=named), args.steps, args.warmup)[1]
     traffic = traffic_from_profile("fp16_2k", None)
     out = {
         "metric": "TFLOP/s and % of MFMA peak, fp16 1024x1024x2048 & mxfp8 1024x2048x4096",
@@ -517,7 +961,20 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK["f16"], 4),
                      "traffic": traffic, "kernel_ms_mean": round(mean_ms, 5),
                      "flop_per_launch": flop,
-                     "timing": "one HIP-graph replay of the timed launches between two events"},
+                     "timing": "one HIP-graph replay of the timed launches between two events",
+                     "sclk_mhz": clk["sclk_mhz_median"],
+                     "frac_at_measured_clock": round(
+                         achieved / (PEAK["f16"] * clk["sclk_mhz_median"] / 2400.0), 4)},
+        "median_of_50": {"us": round(med_ms * 1e3, 3),
+                         "tflops": round(flop / (med_ms * 1e-3) / 1e12, 2),
+                         "timing": "median over 50 launches of the span from the first "
+                                   "workgroup's start to the last one's end (device clock record)"},
+        "clock": clk,
+        "named_tile": {"tile": [256, 128], "swizzle": {"offset": 4, "direction": "zn"},
+                       "us": round(named_per * 1e3, 3),
+                       "tflops": round(flop / (named_per * 1e-3) / 1e12, 2),
+                       "pct_of_peak": round(100.0 * flop / (named_per * 1e-3) / 1e12 / PEAK["f16"], 2),
+                       "note": "32 tiles for 256 CUs: at most 12.5% of the chip busy"},
     }
 
     # ---------------------------------------------------------- MX-fp8 --
@@ -541,6 +998,11 @@ def main():
         tot, mean_x = time_launches(stepx, args.steps, args.warmup)
         fx = 2.0 * Mx * Nx * Kx
         vx = fx * args.steps / (tot * 1e-3) / 1e12
+        medx = median_launch(bst, stepx)
+        clkx = shader_clock(bst, stepx)
+        namedx = bst.make_sched(tile=(256, 256), offset=4, direction="zn")
+        named_x = time_launches(lambda: bst.gemm(Ax, Bx, Cx, scale_a=sa, scale_b=sb, sched=namedx),
+                                args.steps, args.warmup)[1]
         out["mxfp8"] = {
             "workload": "MX-fp8 GEMM M=1024 N=2048 K=4096, e4m3 + e8m0 per-32 scales, bf16 out",
             "value": round(vx, 2), "unit": "TFLOP/s",
@@ -548,7 +1010,17 @@ def main():
             "ms_per_step": round(tot / args.steps, 5),
             "kernel_ms_mean": round(mean_x, 5),
             "achieved": round(fx / (mean_x * 1e-3) / 1e12, 2), "peak": PEAK["e4m3"],
+            "frac": round(fx / (mean_x * 1e-3) / 1e12 / PEAK["e4m3"], 4),
+            "frac_at_measured_clock": round(fx / (mean_x * 1e-3) / 1e12 /
+                                            (PEAK["e4m3"] * clkx["sclk_mhz_median"] / 2400.0), 4),
             "tile": [effx.tile_m, effx.tile_n, effx.tile_k], "split_k": effx.split_k, "shuffle_k": effx.shuffle_k,
+            "median_of_50": {"us": round(medx * 1e3, 3),
+                             "tflops": round(fx / (medx * 1e-3) / 1e12, 2)},
+            "clock": clkx,
+            "named_tile": {"tile": [256, 256], "swizzle": {"offset": 4, "direction": "zn"},
+                           "us": round(named_x * 1e3, 3),
+                           "tflops": round(fx / (named_x * 1e-3) / 1e12, 2),
+                           "pct_of_peak": round(100.0 * fx / (named_x * 1e-3) / 1e12 / PEAK["e4m3"], 2)},
         }
 
     # ---------------------------------------------------- CPU baseline --
@@ -565,7 +1037,7 @@ def main():
             dt = time.perf_counter() - t
             if dt >= 10.0 or reps >= 15:
                 break
-        omp = int(os.environ.get("OMP_NUM_THREADS", cores))
+        omp = oracle.threads()
         # the oracle's result also checks the last timed launch's output
         got = C.cpu().view(torch.int16).numpy().view(np.uint16)
         got = oracle.decode("f16", got if rows is None else got[rows])
@@ -575,7 +1047,7 @@ def main():
             sys.exit(1)
         out["cpu_baseline"] = {
             "value": round(2.0 * nrows * N * K * reps / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": min(omp, cores), "kind": "oracle",
+            "cores": min(omp, cores), "host_cores_visible": cores, "kind": "oracle",
             "sample": "%d x %d of %d output rows of the fp16 1024x1024x2048 workload (fp64 "
                       "oracle, %.2f s)" % (reps, nrows, M, dt),
             "parity_max_norm_err": err,

@@ -25,7 +25,7 @@ _DIRS = {"zn": ZN, "nz": NZ, "raster": RASTER}
 __all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_gemm",
            "grouped_gemm_slice_m", "grouped_gemm_slice_k",
            "quant_gemm_per_token", "tile_map", "grouped_tile_map", "workspace_bytes",
-           "effective_sched", "task_count", "version", "LIB_PATH"]
+           "effective_sched", "task_count", "clock_record", "version", "LIB_PATH"]
 
 
 def make_sched(tile=(0, 0), tile_k=0, offset=1, direction="zn", split_k=1, xcd_remap=0, grid=0,
@@ -67,6 +67,13 @@ def gemm_padded(A, B, C=None, *, out_dtype=None, scale_a=None, scale_b=None, sch
 
 def version():
     return lib().bst_version().decode()
+
+
+def clock_record(buf=None, n=0):
+    """Measurement hook: while set, GEMMs on the LDS-DMA kernels record each of their first n
+    workgroups' clock in buf (an int64 GPU tensor of at least 4 n elements: reference counter
+    at start and end, shader cycles, 1); clock_record() turns it off."""
+    check(lib().bst_set_clock_record(_ptr(buf), n))
 
 
 def _torch():

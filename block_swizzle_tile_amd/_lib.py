@@ -23,7 +23,7 @@ F16, BF16, E4M3, MXE4M3, I8, I32, F32 = 1, 2, 3, 4, 5, 6, 7
 EXPORTS = ["bst_gemm", "bst_gemm_noalloc", "bst_gemm_add", "bst_gemm_padded", "bst_batched_gemm",
            "bst_grouped_gemm_slice_m", "bst_grouped_gemm_slice_k", "bst_quant_gemm_per_token",
            "bst_tile_map", "bst_grouped_tile_map", "bst_workspace_bytes", "bst_effective_sched",
-           "bst_task_count", "bst_last_error", "bst_version"]
+           "bst_task_count", "bst_set_clock_record", "bst_last_error", "bst_version"]
 
 
 class Sched(ctypes.Structure):
@@ -78,6 +78,8 @@ def lib():
                        "bst_quant_gemm_per_token", "bst_tile_map", "bst_grouped_tile_map",
                        "bst_effective_sched", "bst_task_count"):
                 getattr(L, fn).restype = st
+            L.bst_set_clock_record.argtypes = [p, i64]
+            L.bst_set_clock_record.restype = st
             L.bst_last_error.restype = ctypes.c_char_p
             L.bst_version.restype = ctypes.c_char_p
             _lib = L

@@ -20,6 +20,10 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Measurement hook (bst_set_clock_record): device buffer and workgroup count.
+uint64_t* g_clock = nullptr;
+uint32_t g_clock_n = 0;
+
 #ifdef BST_TRACE
 uint64_t* g_trace = nullptr;  // device buffer for the K-loop cycle accounting
 #endif
@@ -304,6 +308,8 @@ void fill_ws(GemmArgs& a, const Plan& p, void* ws) {
 bst_status launch(const Plan& p, const GemmArgs& a, void* stream) {
   GemmArgs b = a;
   b.grid = p.grid;
+  b.clock = g_clock;
+  b.clock_n = g_clock_n;
   const hipError_t e =
       p.inst->launch(dim3(p.grid), dim3(p.inst->threads), (hipStream_t)stream, b);
   if (e != hipSuccess) return fail(BST_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -532,6 +538,14 @@ void bst_debug_set_trace(void* dev_buf) { g_trace = (uint64_t*)dev_buf; }
 #endif
 
 const char* bst_last_error(void) { return g_err; }
+
+bst_status bst_set_clock_record(void* dev_buf, int64_t n) {
+  if (n < 0 || n > 0x7fffffff || (n > 0 && !dev_buf))
+    return fail(BST_E_INVAL, "clock record: n %lld with buffer %p", (long long)n, dev_buf);
+  g_clock = n > 0 ? static_cast<uint64_t*>(dev_buf) : nullptr;
+  g_clock_n = (uint32_t)n;
+  return BST_OK;
+}
 
 const char* bst_version(void) { return "bst 0.1 (gfx950)"; }
 

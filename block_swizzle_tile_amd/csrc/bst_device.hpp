@@ -92,6 +92,34 @@ struct GemmArgs {
   uint32_t tile_cap;                  // tiles the workspace was sized for
   uint32_t* map_out;                  // map-dump kernel only
   uint64_t* trace;                    // BST_TRACE builds only: per-wave cycle counts of workgroup 0
+  uint64_t* clock;                    // measurement hook (null: off): per-workgroup clock record
+  uint32_t clock_n;                   // workgroups recorded (the first clock_n)
+};
+
+// Clock record of a workgroup (LDS-DMA kernels, when a.clock is set):
+// the 100 MHz reference counter at the workgroup's start and end and the
+// shader cycles in between, so that shader cycles / reference ticks is the
+// shader clock it ran at.
+struct ClockMark {
+  uint64_t ref0 = 0, sh0 = 0;
+  __device__ __forceinline__ void start(const GemmArgs& a) {
+    if (a.clock != nullptr) {
+      ref0 = __builtin_amdgcn_s_memrealtime();
+      sh0 = __builtin_amdgcn_s_memtime();
+    }
+  }
+  __device__ __forceinline__ void stop(const GemmArgs& a) {
+    if (a.clock != nullptr && threadIdx.x == 0 && blockIdx.x < a.clock_n) {
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint64_t sh1 = __builtin_amdgcn_s_memtime();
+      const uint64_t ref1 = __builtin_amdgcn_s_memrealtime();
+      uint64_t* o = a.clock + 4 * blockIdx.x;
+      o[0] = ref0;
+      o[1] = ref1;
+      o[2] = sh1 - sh0;
+      o[3] = 1;
+    }
+  }
 };
 
 // ------------------------------------------------------------ scheduler ---

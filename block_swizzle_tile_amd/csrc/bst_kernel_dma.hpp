@@ -874,6 +874,8 @@ struct DmaKernel {
 
   __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
     uint64_t t_start = trace_stamp();
+    ClockMark clk;
+    clk.start(a);
 #ifdef BST_TRACE
     const uint64_t clk_ref0 = __builtin_amdgcn_s_memrealtime();
     const uint64_t clk_sh0 = t_start;
@@ -995,6 +997,7 @@ struct DmaKernel {
       t_start = trace_stamp();
     }
     if (dyn && threadIdx.x == 0) queue_exit(a);
+    clk.stop(a);
 #ifdef BST_TRACE
     // Clock record of the first 256 workgroups at trace[128 + 4 w]: the
     // 100 MHz reference counter at the start and at the end, and the shader

@@ -350,6 +350,17 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
 bst_status bst_task_count(int kind, bst_dtype ab, int64_t count, int64_t M, int64_t N,
                           const bst_sched* sched, int64_t* tasks);
 
+/* bst_set_clock_record -- measurement hook for the shader clock a GEMM runs
+ * at.  While set (n > 0), every GEMM launched on the LDS-DMA kernels makes
+ * each of its first n workgroups record, at dev_buf[4w .. 4w+3] (uint64,
+ * device memory of at least 32 n bytes), the 100 MHz reference counter at
+ * the workgroup's start and end, its shader cycles in between, and 1; the
+ * shader clock is cycles / ((end - start) / 100 MHz).  n = 0 turns it off
+ * (the kernels then only test a null pointer).  Process-wide: set it from
+ * one thread while no GEMM is being enqueued.  BST_E_INVAL for n < 0 or a
+ * NULL buffer with n > 0. */
+bst_status bst_set_clock_record(void* dev_buf, int64_t n);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* bst_last_error(void);
 

@@ -71,6 +71,8 @@ def lib():
             L.orc_grouped_gemm_slice_k.restype = ctypes.c_int
             L.orc_add_addend.argtypes = [i64, p, p, p]
             L.orc_add_addend.restype = ctypes.c_int
+            L.orc_threads.argtypes = [ctypes.c_int]
+            L.orc_threads.restype = ctypes.c_int
             L.orc_compare.argtypes = [i64, p, p, p, p]
             L.orc_compare.restype = dbl
             _lib = L
@@ -216,6 +218,11 @@ def gemm_add(ab, A, B, X, x_kind, **kw):
     if lib().orc_add_addend(ref.size, _ptr(x), _ptr(ref), _ptr(den)) != 0:
         raise ValueError("orc_add_addend failed")
     return ref, den
+
+
+def threads(n=0):
+    """OpenMP thread count of the oracle's loops: n > 0 sets it; returns the count in use."""
+    return lib().orc_threads(int(n))
 
 
 def compare(got, ref, den):

@@ -519,6 +519,24 @@ int orc_add_addend(int64_t n, const double *x, double *ref, double *den) {
   return 0;
 }
 
+/* ----------------------------------------------------------- threads ---- */
+
+/* Thread count of the OpenMP loops above: n > 0 sets it, n <= 0 only asks.
+ * Returns the count the next parallel loop will use (no arithmetic here;
+ * the CPU-baseline timing reports it as its core count). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* ---------------------------------------------------------- compare ----- */
 
 /*
