@@ -277,6 +277,12 @@ int kind_form(int kind) {
   return kind == 1 ? FORM_SLICE_M : kind == 3 ? FORM_SLICE_K : FORM_DENSE;
 }
 
+// The map's launch constants for a problem of M x N per batch / group.
+MapConsts map_consts(const Plan& p, int64_t M, int64_t N) {
+  return make_map_consts((uint32_t)cdiv64(M, p.bm), (uint32_t)cdiv64(N, p.bn), p.off, p.dir,
+                         (uint32_t)p.tile_cap, p.bk ? p.kslice / p.bk : 0u);
+}
+
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 bool stride_ok(int64_t ld, size_t es) { return ((uint64_t)ld * es) % 16 == 0; }
 
@@ -387,6 +393,7 @@ bst_status prepare_dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, in
   a.batch = (uint32_t)batch;
   a.tiles = (uint32_t)p.tile_cap;
   a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
+  a.mc = map_consts(p, M, N);
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
   empty = false;
@@ -717,6 +724,7 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
   a.total_m = total_m;
   a.N = (uint32_t)N; a.K = (uint32_t)K;
   a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
+  a.mc.nk_full = make_fastdiv(p.bk ? p.kslice / p.bk : 1u);  // the map itself is per group
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
   return launch(p, a, stream);
@@ -776,6 +784,8 @@ bst_status bst_grouped_gemm_slice_k(bst_dtype ab, bst_dtype c, int32_t G, const 
   a.batch = (uint32_t)G;
   a.tiles = (uint32_t)p.tile_cap;
   a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
+  a.mc = map_consts(p, M, N);
+  a.mc.nk_full = make_fastdiv(1);  // groups differ in K: ShuffleK does not apply
   a.cdtype = (uint32_t)c;
   fill_ws(a, p, ws);
   return launch(p, a, stream);
@@ -802,6 +812,7 @@ bst_status bst_tile_map(bst_dtype ab, int64_t batch, int64_t M, int64_t N, const
   a.batch = (uint32_t)batch;
   a.tiles = (uint32_t)p.tile_cap;
   a.off = p.off; a.dir = p.dir; a.remap = p.remap; a.shuffle_k = p.shuffle;
+  a.mc = map_consts(p, M, N);
   a.map_out = out;
   uint32_t grid = s && s->grid ? std::min<uint32_t>(s->grid, a.tiles)
                                : (uint32_t)std::min<int64_t>(device_cus(), a.tiles);

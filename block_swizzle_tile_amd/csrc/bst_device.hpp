@@ -54,6 +54,46 @@ typedef __attribute__((address_space(3))) uint8_t lds_byte_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_out_t;
 
 // ------------------------------------------------------------ arguments ---
+// Division of 32-bit unsigned values by a divisor fixed for a launch,
+// without a division instruction: q = (mulhi(n, mul) + n) >> shift with the
+// multiplier and shift precomputed on the host (the round-up reciprocal
+// method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  Exact for every n < 2^32 and 1 <= d < 2^31.
+struct FastDiv {
+  uint32_t d, mul, shift;
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t hi = __umulhi(n, mul);
+#else
+    const uint32_t hi = (uint32_t)(((uint64_t)n * mul) >> 32);
+#endif
+    return (uint32_t)(((uint64_t)hi + n) >> shift);
+  }
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0u, 0u};
+  if (d == 0) return f;
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;  // l = ceil(log2 d)
+  f.shift = l;
+  f.mul = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+  return f;
+}
+
+// The block map of one launch with fixed loop counts (plain, batched and
+// slice-K problems), precomputed on the host: the window order of
+// GetBlockCoord ("Block Scheduler Code Explained", s4.5) reduced to
+// multiplications.  The direction's major dimension is cut into W windows
+// of o tile-lines (the last one holds `last`); span = o x (tile-lines of the
+// minor dimension).  RASTER is the Nz order with one window spanning every
+// column (offset >= loopsN), which walks the tiles row by row.
+struct MapConsts {
+  uint32_t nz;        // 0: windows of tile-rows (Zn); 1: of tile-columns (Nz, RASTER)
+  uint32_t o, W, last, loops_min;
+  FastDiv span, by_o, by_last, core, tiles, nk_full;
+};
+
 struct GemmArgs {
   const uint8_t* A;
   const uint8_t* B;
@@ -90,6 +130,7 @@ struct GemmArgs {
   float* ws_part;                     // split > 1: [split][tile capacity][BM*BN] partials
   uint32_t* ws_count;                 // split > 1: one arrival counter per tile
   uint32_t tile_cap;                  // tiles the workspace was sized for
+  MapConsts mc;                       // plain, batched, slice-K: the map's constants
   uint32_t* map_out;                  // map-dump kernel only
   uint64_t* trace;                    // BST_TRACE builds only: per-wave cycle counts of workgroup 0
   uint64_t* clock;                    // measurement hook (null: off): per-workgroup clock record
@@ -158,6 +199,21 @@ __host__ __device__ __forceinline__ TileCoord block_coord(uint32_t loopsM, uint3
     c.m = inner / loopsN;
     c.n = inner - c.m * loopsN;
   }
+  return c;
+}
+
+// block_coord with the launch's precomputed constants (same results).
+__host__ __device__ __forceinline__ TileCoord block_coord_fast(const MapConsts& mc, uint32_t inner) {
+  const uint32_t w = mc.span.div(inner);
+  const uint32_t j = inner - w * mc.span.d;
+  const bool tail = w == mc.W - 1;
+  const uint32_t q = tail ? mc.by_last.div(j) : mc.by_o.div(j);
+  const uint32_t rows = tail ? mc.last : mc.o;
+  const uint32_t maj = w * mc.o + (j - q * rows);
+  const uint32_t mnr = (w & 1u) ? mc.loops_min - 1 - q : q;  // snake (s5.2)
+  TileCoord c;
+  c.m = mc.nz ? mnr : maj;
+  c.n = mc.nz ? maj : mnr;
   return c;
 }
 
@@ -259,13 +315,14 @@ __host__ __device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t
     inner = t - gt->first_task[lo];
     Mp = (uint32_t)(gt->first_row[lo + 1] - gt->first_row[lo]);
   } else {
-    const uint32_t core = ((a.M + BM - 1) / BM) * loopsN;  // s4.3 GetCoreLoops
-    k.idx = t / core;                                      // s4.4 GetBatchIdx
+    const uint32_t core = a.mc.core.d;  // s4.3 GetCoreLoops: loopsM * loopsN
+    k.idx = a.mc.core.div(t);           // s4.4 GetBatchIdx
     inner = t - k.idx * core;
     Mp = a.M;
   }
   const uint32_t loopsM = (Mp + BM - 1) / BM;
-  const TileCoord c = block_coord(loopsM, loopsN, a.off, a.dir, inner);
+  const TileCoord c = gt ? block_coord(loopsM, loopsN, a.off, a.dir, inner)
+                         : block_coord_fast(a.mc, inner);
   k.m = c.m;
   k.n = c.n;
   k.mAct = (c.m == loopsM - 1) ? Mp - c.m * BM : BM;  // s4.6 GetActualBlockShape
@@ -279,6 +336,29 @@ __host__ __device__ __forceinline__ Task decode_task(const GemmArgs& a, uint32_t
     k.rows_valid = k.mAct;
   }
   return k;
+}
+
+// MapConsts of a problem with loopsM x loopsN tiles per batch / group,
+// `tiles` tasks in all and nk_full stages in a full K slice.
+inline MapConsts make_map_consts(uint32_t loopsM, uint32_t loopsN, uint32_t off, uint32_t dir,
+                                 uint32_t tiles, uint32_t nk_full) {
+  MapConsts mc{};
+  const bool nz = dir != 0;
+  const uint32_t maj = nz ? loopsN : loopsM, mnr = nz ? loopsM : loopsN;
+  uint32_t o = dir == 2 ? maj : (off < maj ? off : maj);  // RASTER: one window
+  if (o == 0) o = 1;
+  mc.nz = nz ? 1u : 0u;
+  mc.o = o;
+  mc.W = maj == 0 ? 1u : (maj + o - 1) / o;
+  mc.last = maj == 0 ? o : maj - o * (mc.W - 1);
+  mc.loops_min = mnr;
+  mc.span = make_fastdiv(o * (mnr ? mnr : 1u));
+  mc.by_o = make_fastdiv(o);
+  mc.by_last = make_fastdiv(mc.last ? mc.last : 1u);
+  mc.core = make_fastdiv(loopsM * loopsN ? loopsM * loopsN : 1u);
+  mc.tiles = make_fastdiv(tiles ? tiles : 1u);
+  mc.nk_full = make_fastdiv(nk_full ? nk_full : 1u);
+  return mc;
 }
 
 // Workgroup renumbering: hardware places workgroup w on XCD w % 8; with

@@ -755,7 +755,7 @@ struct DmaKernel {
   __device__ static __forceinline__ void setup_unit(const GemmArgs& a, const GroupTable* gt,
                                                     uint32_t T_tiles, uint32_t u, Unit& un,
                                                     Ctx& c) {
-    un.s = u / T_tiles;
+    un.s = GROUPED ? u / T_tiles : a.mc.tiles.div(u);
     un.t = u - un.s * T_tiles;
     Task tk = decode_task(a, un.t, BM, BN, GROUPED ? gt : nullptr);
     if constexpr (GROUPED) {
@@ -794,8 +794,10 @@ struct DmaKernel {
     c.k0 = k0;
     c.kend = k1;
     un.whole = un.nk > 0 && full_task(k0, k1);
-    c.kshift = (a.shuffle_k != 0 && un.whole) ? un.t % un.nk : 0u;
-    c.nks = (a.shuffle_k != 0 && un.whole) ? un.nk : 0xFFFFFFFFu;
+    // ShuffleK: tasks of the launch's full stage count S start at stage t mod S
+    const bool shuffle = a.shuffle_k != 0 && un.whole && un.nk == a.mc.nk_full.d;
+    c.kshift = shuffle ? un.t - a.mc.nk_full.div(un.t) * un.nk : 0u;
+    c.nks = shuffle ? un.nk : 0xFFFFFFFFu;
     lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
                c.ldb_bytes, a.ldsa, a.ldsb);
     un.tk = tk;

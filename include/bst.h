@@ -83,9 +83,11 @@ typedef struct bst_sched {
                                   "Block Dispatch Policies"): the K loop of task t starts at
                                   stage t mod S of its S stages and wraps around, so that tiles
                                   running together read different K slices.  Applied by the
-                                  LDS-DMA family to tasks of whole stages; others run in order.
-                                  0 = off.  Results differ from 0 only by fp32 summation order
-                                  (int8: bit-identical). */
+                                  LDS-DMA family to tasks of whole stages whose count is the
+                                  launch's full slice (not to a shorter last slice, nor to
+                                  slice-K groups); others run in order.  0 = off.  Results
+                                  differ from 0 only by fp32 summation order (int8:
+                                  bit-identical). */
   uint32_t dynamic;            /* 1: dynamic task allocation ("Block Scheduler Code Explained",
                                   s1): after a first round of one unit per workgroup, the
                                   units go to eight queues, one per XCD; each workgroup takes

@@ -89,6 +89,9 @@ void check(const Problem& p) {
   } else {
     T = (uint32_t)(p.batch * ((p.M + BM - 1) / BM) * loopsN);
   }
+  if (!GROUPED)
+    a.mc = make_map_consts((uint32_t)((p.M + BM - 1) / BM), loopsN, a.off, a.dir, T,
+                           (uint32_t)(kslice / BK));
   const int64_t rowbytesA = p.lda * ES, rowbytesB = p.ldb * ES;
   for (uint32_t s = 0; s < split; ++s) {
     for (uint32_t t = 0; t < T; ++t) {
@@ -316,7 +319,52 @@ void run_slicek(const std::vector<Problem>& ps) {
   for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, FORM_SLICE_K>(p);
 }
 
+// The division by invariant integers against the hardware-free '/': every
+// divisor up to 4096 and a spread of larger ones, each with the dividends
+// that sit at and around its multiples and at the ends of the range.
+static void check_fastdiv() {
+  std::vector<uint32_t> ds;
+  for (uint32_t d = 1; d <= 4096; ++d) ds.push_back(d);
+  for (uint64_t d = 4097; d < (1ull << 31); d = d * 3 / 2 + 7) ds.push_back((uint32_t)d);
+  ds.push_back(0x7fffffffu);
+  uint64_t x = 88172645463325252ull;  // xorshift for pseudo-random dividends
+  for (uint32_t d : ds) {
+    const FastDiv f = make_fastdiv(d);
+    std::vector<uint32_t> ns = {0u, 1u, d - 1, d, d + 1, 0xffffffffu, 0xfffffffeu, 0x80000000u};
+    for (uint32_t k = 1; k < 64; ++k) {
+      const uint64_t m = (uint64_t)d * k * 977u;
+      if (m <= 0xffffffffull) { ns.push_back((uint32_t)m); ns.push_back((uint32_t)(m - 1)); }
+      x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+      ns.push_back((uint32_t)x);
+    }
+    for (uint32_t n : ns) {
+      ++g_checked;
+      REQUIRE(f.div(n) == n / d, "fastdiv %u / %u = %u", n, d, f.div(n));
+    }
+  }
+}
+
+// The map with the launch's precomputed constants against block_coord (the
+// reference the GPU map test pins to the oracle) over every task.
+static void check_fast_map() {
+  for (uint32_t lm = 1; lm <= 37; ++lm)
+    for (uint32_t ln = 1; ln <= 37; ln += (ln < 12 ? 1 : 5))
+      for (uint32_t off : {1u, 2u, 3u, 4u, 5u, 8u, 13u, 1000u})
+        for (uint32_t dir = 0; dir < 3; ++dir) {
+          const MapConsts mc = make_map_consts(lm, ln, off, dir, lm * ln, 1);
+          for (uint32_t i = 0; i < lm * ln; ++i) {
+            const TileCoord r = block_coord(lm, ln, off, dir, i);
+            const TileCoord f = block_coord_fast(mc, i);
+            ++g_checked;
+            REQUIRE(r.m == f.m && r.n == f.n, "map %ux%u off %u dir %u task %u: (%u,%u) vs (%u,%u)",
+                    lm, ln, off, dir, i, r.m, r.n, f.m, f.n);
+          }
+        }
+}
+
 int main() {
+  check_fastdiv();
+  check_fast_map();
   // 16-bit operands: K and N multiples of 8 elements
   const std::vector<Problem> p16 = {
       plain("tails", 200, 136, 256, 0, 0, 1),      plain("tails-split", 200, 136, 256, 8, 16, 3),
