@@ -819,6 +819,13 @@ def phases(args, torch, np, I, gpu):
     C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
     s = bst.make_sched(tile=(64, 64), offset=8, direction="zn", xcd_remap=1, shuffle_k=1)
     one("C2 fp16 1024x1024x2048 64x64", lambda: bst.gemm(A, B, C, sched=s))
+    # larger tiles cut each unit's operand bytes; split-K brings the unit count back to the
+    # CU count, at the price of the partial tiles' fix-up
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for tile, split in [((128, 128), 4), ((128, 128), 1), ((64, 64), 2), ((256, 128), 8)]:
+        ss = bst.make_sched(tile=tile, offset=4, direction="zn", xcd_remap=1, split_k=split)
+        one("C2 fp16 1024x1024x2048 %dx%d split %d" % (tile + (split,)),
+            lambda: bst.gemm(A, B, C, sched=ss, workspace=ws))
     x = I.workload("mxfp8_4k")
     Ax, Bx = gpu(x["A"], "e4m3"), gpu(x["B"], "e4m3")
     sa, sb = gpu(x["scale_a"], "u8"), gpu(x["scale_b"], "u8")

@@ -11,7 +11,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libbst.so")
+# BST_LIB selects another build of the same library (the sanitizer build of the
+# CPU tests); there is no other library and no fallback
+LIB_PATH = os.environ.get("BST_LIB") or os.path.join(PKG, "libbst.so")
 
 # bst_status
 OK, E_INVAL, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5

@@ -61,8 +61,8 @@ size_t elem_size(bst_dtype t) {
     case BST_I8: return 1;
     case BST_I32:
     case BST_F32: return 4;
+    default: return 0;  // not a dtype
   }
-  return 0;
 }
 
 bool is_ab(bst_dtype t) {

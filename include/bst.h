@@ -54,7 +54,11 @@ typedef enum bst_dtype {
   BST_MXE4M3 = 4,  /* OCP FP8 E4M3 with one E8M0 scale per 32 consecutive K values */
   BST_I8 = 5,      /* int8 */
   BST_I32 = 6,     /* int32 (raw int8 accumulators) */
-  BST_F32 = 7      /* binary32 */
+  BST_F32 = 7,     /* binary32 */
+  /* not dtypes: they make every int32 value a valid bst_dtype, so that the
+     library can read and reject any value a caller passes */
+  BST_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  BST_DTYPE_RANGE_MAX_ = 2147483647
 } bst_dtype;
 
 typedef enum bst_direction {

@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects a prebuilt copy (the sanitizer build of the CPU tests), used as is
+_LIB_ENV = os.environ.get("ORACLE_LIB")
+_LIB = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -38,6 +40,8 @@ _DECODE_KIND = {"f16": 1, "bf16": 2, "e4m3": 3, "i8": 5, "i32": 6, "f32": 7, "e8
 
 def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (OpenMP)."""
+    if _LIB_ENV:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-shared",
