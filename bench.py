@@ -704,9 +704,16 @@ def large(args, bst, torch):
                                   "error": repr(ex)[:200]}), flush=True)
                 continue
             tf = flop / (ms * 1e-3) / 1e12
-            print(json.dumps({"shape": [M, N, K], "dtype": wl, "impl": name,
-                              "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 1),
-                              "pct_of_peak": round(100.0 * tf / peak, 1)}), flush=True)
+            rec = {"shape": [M, N, K], "dtype": wl, "impl": name,
+                   "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                   "pct_of_peak": round(100.0 * tf / peak, 1)}
+            if name.startswith("bst"):
+                # the production kernel's own clock record (bst_set_clock_record)
+                clk = shader_clock(bst, fn)
+                rec["sclk_mhz"] = clk["sclk_mhz_median"]
+                rec["pct_at_measured_clock"] = round(
+                    100.0 * tf / (peak * clk["sclk_mhz_median"] / 2400.0), 1)
+            print(json.dumps(rec), flush=True)
         del A, B, C, kw
 
 
