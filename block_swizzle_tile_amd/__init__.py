@@ -31,7 +31,8 @@ __all__ = ["Sched", "BstError", "make_sched", "gemm", "gemm_padded", "batched_ge
 def make_sched(tile=(0, 0), tile_k=0, offset=1, direction="zn", split_k=1, xcd_remap=0, grid=0,
                path=0, shuffle_k=0, dynamic=0, preload=0):
     """A :class:`Sched` from Python values (direction: 'zn', 'nz', 'raster' or 0/1/2;
-    path: 0 automatic, 1 register-staged kernels, 2 LDS-DMA kernels; shuffle_k: 1 rotates
+    path: 0 automatic, 1 register-staged kernels, 2 LDS-DMA kernels, 3 LDS-DMA kernels with
+    two resident workgroups per CU; shuffle_k: 1 rotates
     each task's K-loop start; dynamic: 1 per-XCD work queues; preload: 1 issues the next
     task's first stages before the current epilogue)."""
     d = _DIRS[direction] if isinstance(direction, str) else int(direction)

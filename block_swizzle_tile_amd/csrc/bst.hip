@@ -39,14 +39,14 @@ bst_status fail(bst_status st, const char* fmt, ...) {
 int kernel_ab(bst_dtype ab) { return (int)ab; }
 
 const Instance* find_instance(bst_dtype ab, uint32_t bm, uint32_t bn, int form, bool dma,
-                              bool add = false) {
+                              bool add = false, int wgs = 1) {
   const InstanceList lists[] = {instances_f16(), instances_bf16(), instances_i8(),
                                 instances_fp8(), instances_mxfp8(), instances_slicek()};
   for (const InstanceList& l : lists)
     for (int i = 0; i < l.count; ++i) {
       const Instance& in = l.begin[i];
       if (in.ab == kernel_ab(ab) && (uint32_t)in.bm == bm && (uint32_t)in.bn == bn &&
-          in.form == form && in.dma == dma && in.add == add)
+          in.form == form && in.dma == dma && in.add == add && in.wgs == wgs)
         return &in;
     }
   return nullptr;
@@ -192,14 +192,16 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
     d.tile_m = 128;
     d.tile_n = 128;
   }
-  if (d.path > 2) return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma}", d.path);
+  if (d.path > 3)
+    return fail(BST_E_INVAL, "path %u not in {0 auto, 1 register, 2 dma, 3 dma pair}", d.path);
   if (d.shuffle_k > 1) return fail(BST_E_INVAL, "shuffle_k must be 0 or 1");
   if (d.dynamic > 1) return fail(BST_E_INVAL, "dynamic must be 0 or 1");
   if (d.preload > 1) return fail(BST_E_INVAL, "preload must be 0 or 1");
   // matmul-add runs only the LDS-DMA instances built with the addend epilogue
   const Instance* reg = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, form, false);
   const Instance* dma = find_instance(ab, d.tile_m, d.tile_n, form, true, add);
-  if (!reg && !dma)
+  const Instance* pair = add ? nullptr : find_instance(ab, d.tile_m, d.tile_n, form, true, false, 2);
+  if (!reg && !dma && !pair)
     return fail(BST_E_UNSUPPORTED, "no %s kernel for dtype %d with tile %ux%u",
                 add ? "matmul-add" : form == FORM_SLICE_M ? "grouped slice-M"
                 : form == FORM_SLICE_K ? "grouped slice-K" : "plain", (int)ab, d.tile_m,
@@ -209,11 +211,16 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
   // so the total K need not be whole chunks
   const int64_t ce = 16 / (int64_t)elem_size(ab);
   const int64_t kfit = form == FORM_SLICE_K ? (K + ce - 1) / ce * ce : K;
-  const bool fits = dma && dma_fits(ab, N, kfit, d.tile_m, (uint32_t)dma->bk, lay);
-  if (d.path == 2 && !fits)
+  const Instance* any_dma = dma ? dma : pair;  // both run the same stage depth (bk)
+  const bool fits = any_dma && dma_fits(ab, N, kfit, d.tile_m, (uint32_t)any_dma->bk, lay);
+  if ((d.path == 2 || d.path == 3) && !fits)
     return fail(BST_E_UNSUPPORTED, "the LDS-DMA kernels need K and N in whole 16-byte chunks "
                 "(and K %% 128 == 0 for MX); use path 0 or 1");
-  p.inst = (d.path == 1 || !fits) ? reg : dma;
+  if (d.path == 3 && !pair)
+    return fail(BST_E_UNSUPPORTED, "no two-workgroup LDS-DMA kernel for dtype %d with tile %ux%u "
+                "in this problem form", (int)ab, d.tile_m, d.tile_n);
+  // path 0 decides between dma and pair below, once the unit count is known
+  p.inst = (d.path == 1 || !fits) ? reg : d.path == 3 ? pair : (dma ? dma : pair);
   if (!p.inst) return fail(BST_E_UNSUPPORTED, "no kernel of the requested family for this tile");
   if (d.tile_k != 0 && d.tile_k != (uint32_t)p.inst->bk)
     return fail(BST_E_UNSUPPORTED, "tile_k %u: this dtype runs tile_k %d", d.tile_k,
@@ -253,6 +260,11 @@ bst_status make_plan(int form, bst_dtype ab, int64_t count, int64_t M, int64_t N
   if (kslice_steps > 0 && form != FORM_SLICE_K) split = cdiv64(nk, kslice_steps);
   p.split = (uint32_t)split;
   p.kslice = (uint32_t)(kslice_steps * p.bk);
+  // automatic family: two resident workgroups per CU when the launch has
+  // more units than CUs (one workgroup's epilogue and set-up then overlap
+  // the other's K loop), one deeper-pipelined workgroup otherwise
+  if (d.path == 0 && p.inst->dma && pair && dma)
+    p.inst = tiles * split > (int64_t)cus ? pair : dma;
   if (tiles * split > kMaxU32) return fail(BST_E_INVAL, "work-unit count above 2^31-1");
   if (p.split > 1) {
     if (tiles > (int64_t)kMaxSplitTiles)
@@ -898,7 +910,7 @@ bst_status bst_effective_sched(int kind, bst_dtype ab, int64_t count, int64_t M,
   out->split_k = p.split;
   out->xcd_remap = p.remap;
   out->grid = p.grid;
-  out->path = p.inst->dma ? 2u : 1u;
+  out->path = !p.inst->dma ? 1u : p.inst->wgs == 2 ? 3u : 2u;
   out->shuffle_k = p.shuffle;
   out->dynamic = p.dynamic;
   out->preload = p.preload;

@@ -23,6 +23,7 @@ struct Instance {
   int threads;
   int bk;
   bool add = false;  // matmul-add epilogue (C = A.B + X)
+  int wgs = 1;       // resident workgroups per CU it is built for (2: gemm_dma_kernel_pair)
 };
 
 struct InstanceList {
@@ -53,6 +54,20 @@ hipError_t launch_dma(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) 
     AB, BM, BN, GR, true, S,                                                              \
         reinterpret_cast<const void*>(&gemm_dma_kernel<AB, BM, BN, WM, WN, S, GR>),       \
         &launch_dma<AB, BM, BN, WM, WN, S, GR>, 64 * WM * WN, Traits<AB>::BK              \
+  }
+
+template <int AB, int BM, int BN, int WM, int WN, int S, int GR>
+hipError_t launch_dma_pair(dim3 grid, dim3 block, hipStream_t st, const GemmArgs& a) {
+  hipLaunchKernelGGL((gemm_dma_kernel_pair<AB, BM, BN, WM, WN, S, GR>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// An LDS-DMA instance built for two resident workgroups per CU.
+#define BST_DMA_PAIR(AB, BM, BN, WM, WN, S, GR)                                           \
+  Instance {                                                                              \
+    AB, BM, BN, GR, true, S,                                                              \
+        reinterpret_cast<const void*>(&gemm_dma_kernel_pair<AB, BM, BN, WM, WN, S, GR>),  \
+        &launch_dma_pair<AB, BM, BN, WM, WN, S, GR>, 64 * WM * WN, Traits<AB>::BK, false, 2 \
   }
 
 // A matmul-add instance of the LDS-DMA family (plain GEMM only).

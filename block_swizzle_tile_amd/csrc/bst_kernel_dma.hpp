@@ -1027,4 +1027,19 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmArgs a) {
 #endif
 }
 
+// The same kernel built for two resident workgroups per CU: its waves may
+// use at most half of a SIMD's registers (256 per lane, so two waves share
+// each SIMD), and its instances take two pipeline stages, so two
+// workgroups' LDS fits in one CU.  While one workgroup stores a tile or sets
+// up its next one, the other's K loop keeps the CU's loads and matrix cores
+// busy; the host sizes the persistent grid from the occupancy the runtime
+// reports.
+template <int AB, int BM, int BN, int WM, int WN, int STAGES, int FORM>
+__global__ void __launch_bounds__(64 * WM * WN)
+    __attribute__((amdgpu_waves_per_eu(2 * WM * WN / 4))) gemm_dma_kernel_pair(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  DmaKernel<AB, BM, BN, WM, WN, STAGES, FORM, false>::run(a);
+#endif
+}
+
 }  // namespace bst

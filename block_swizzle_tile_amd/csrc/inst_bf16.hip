@@ -15,6 +15,9 @@ static const Instance kList[] = {
     BST_DMA(AB_BF16, 256, 256, 4, 2, 2, FORM_DENSE),
     BST_DMA(AB_BF16, 128, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_BF16, 64, 128, 2, 2, 4, FORM_DENSE),
     BST_DMA_ADD(AB_BF16, 64, 64, 2, 2, 4), BST_DMA_ADD(AB_BF16, 128, 128, 2, 2, 4),
+    // two resident workgroups per CU, two stages
+    BST_DMA_PAIR(AB_BF16, 128, 128, 2, 2, 2, FORM_DENSE),
+    BST_DMA_PAIR(AB_BF16, 128, 128, 2, 2, 2, FORM_SLICE_M),
 };
 
 InstanceList instances_bf16() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }

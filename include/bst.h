@@ -80,9 +80,19 @@ typedef struct bst_sched {
                                   renumbered so that each XCD (accelerator die, own L2)
                                   takes a contiguous range of task indices */
   uint32_t grid;               /* persistent workgroups; 0 = fill every CU */
-  uint32_t path;               /* kernel family: 0 = automatic, 1 = register-staged (any shape),
-                                  2 = LDS-DMA pipeline (K and N whole 16-byte chunks, MX K a
-                                  multiple of 128; BST_E_UNSUPPORTED otherwise) */
+  uint32_t path;               /* kernel family: 1 = register-staged (any shape);
+                                  2 = LDS-DMA pipeline, one workgroup per CU with a deep
+                                  pipeline (K and N whole 16-byte chunks, MX K a multiple of
+                                  128; BST_E_UNSUPPORTED otherwise); 3 = LDS-DMA pipeline with
+                                  two resident workgroups per CU and two stages, so that one
+                                  workgroup's epilogue and set-up overlap the other's K loop
+                                  (fp16 / bf16 / int8 at 128x128, plain, batched and grouped
+                                  slice-M; BST_E_UNSUPPORTED otherwise); 0 = automatic: path 1
+                                  when the layout rules out the LDS-DMA family, else path 3
+                                  where it exists and the launch has more work units than CUs,
+                                  else path 2.  Paths 2 and 3 add the same products in the
+                                  same order: their results are bit-identical (up to the sign
+                                  of an exactly zero floating-point sum). */
   uint32_t shuffle_k;          /* 1: ShuffleK (a policy flag of the Preload dispatch policies,
                                   "Block Dispatch Policies"): the K loop of task t starts at
                                   stage t mod S of its S stages and wraps around, so that tiles

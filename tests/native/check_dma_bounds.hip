@@ -387,6 +387,9 @@ int main() {
   run_plain<AB_F16, 64, 64, 2, 2, 6>(p16);
   run_plain<AB_F16, 64, 64, 2, 2, 5>(p16);
   run_grouped<AB_F16, 128, 128, 2, 2, 4>(g16);
+  // the two-workgroups-per-CU instances (two stages)
+  run_plain<AB_F16, 128, 128, 2, 2, 2>(p16);
+  run_grouped<AB_F16, 128, 128, 2, 2, 2>(g16);
   // slice-K: aligned groups (8 elements), an empty one, a group cut short by
   // the allocation, and groups that break the 16-byte chunks (no access)
   const std::vector<Problem> k16 = {slicek("k16", {64, 0, 200, 8, 136}, 16, 129, 264, 1),
@@ -413,6 +416,8 @@ int main() {
   run_grouped<AB_I8, 128, 128, 2, 2, 4>(g8);
   run_grouped<AB_I8, 256, 128, 2, 2, 3>(g8);
   run_grouped<AB_I8, 256, 256, 4, 2, 2>(g8);
+  run_plain<AB_I8, 128, 128, 2, 2, 2>(p8);
+  run_grouped<AB_I8, 128, 128, 2, 2, 2>(g8);
   const std::vector<Problem> k8 = {
       slicek("k8", {336, 208, 32, 80, 16, 512, 912, 1536}, 0, 200, 144, 1),
       slicek("k8s", {336, 208, 32, 80, 16, 512, 912, 1536}, 32, 64, 256, 3),

@@ -117,8 +117,41 @@ def test_effective_sched_split_resolution(L):
     assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 60,
                                  ctypes.byref(S(tile=(64, 64), path=2)),
                                  ctypes.byref(out)) == _lib.E_UNSUPPORTED
-    assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 64, ctypes.byref(S(path=3)),
+    assert L.bst_effective_sched(0, _lib.F16, 1, 64, 64, 64, ctypes.byref(S(path=4)),
                                  ctypes.byref(out)) == _lib.E_INVAL
+
+
+def test_two_workgroup_family_selection(L):
+    """path 3 (two resident workgroups per CU): chosen automatically at 128x128 when the launch
+    has more units than CUs, on request otherwise; refused where no such instance exists."""
+    out = _lib.Sched()
+
+    def eff(kind, ab, count, M, N, K, **kw):
+        st = L.bst_effective_sched(kind, ab, count, M, N, K, ctypes.byref(S(**kw)),
+                                   ctypes.byref(out))
+        return st, out.path
+    # 1024 tiles of 128x128: more units than CUs
+    for ab in (_lib.F16, _lib.BF16, _lib.I8):
+        assert eff(0, ab, 1, 4096, 4096, 256, tile=(128, 128)) == (_lib.OK, 3)
+        assert eff(0, ab, 1, 4096, 4096, 256, tile=(128, 128), path=2) == (_lib.OK, 2)
+        # 64 tiles: one workgroup per CU with the deeper pipeline, unless asked
+        assert eff(0, ab, 1, 1024, 1024, 256, tile=(128, 128)) == (_lib.OK, 2)
+        assert eff(0, ab, 1, 1024, 1024, 256, tile=(128, 128), path=3) == (_lib.OK, 3)
+        # grouped slice-M
+        assert eff(1, ab, 8, 8192, 4096, 2048, tile=(128, 128)) == (_lib.OK, 3)
+    # batched: 16 x 4 x 6 = 384 tiles
+    assert eff(0, _lib.BF16, 16, 512, 768, 1024, tile=(128, 128)) == (_lib.OK, 3)
+    # a split that brings the units above the CU count
+    assert eff(0, _lib.F16, 1, 1024, 1024, 2048, tile=(128, 128), split_k=8) == (_lib.OK, 3)
+    # no such instance: other tiles, slice-K, MX, matmul-add
+    assert eff(0, _lib.F16, 1, 4096, 4096, 256, tile=(64, 64), path=3)[0] == _lib.E_UNSUPPORTED
+    assert eff(0, _lib.F16, 1, 4096, 4096, 256, tile=(64, 64)) == (_lib.OK, 2)
+    assert eff(3, _lib.I8, 8, 1024, 2048, 8192, tile=(128, 128), path=3)[0] == _lib.E_UNSUPPORTED
+    assert eff(3, _lib.I8, 8, 1024, 2048, 8192, tile=(128, 128)) == (_lib.OK, 2)
+    assert eff(0, _lib.MXE4M3, 1, 4096, 4096, 256, tile=(128, 128)) == (_lib.OK, 2)
+    # a layout the LDS-DMA family cannot take: the register-staged family, and path 3 refused
+    assert eff(0, _lib.F16, 1, 4096, 4096, 250, tile=(128, 128)) == (_lib.OK, 1)
+    assert eff(0, _lib.F16, 1, 4096, 4096, 250, tile=(128, 128), path=3)[0] == _lib.E_UNSUPPORTED
 
 
 def test_gemm_add_validation(L):
