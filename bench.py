@@ -346,9 +346,12 @@ def sweep_configs(args, bst, I, gpu, torch):
         ("C3", dict(tile=[64, 128], offset=8, direction="zn", xcd_remap=1)),
         ("C4", dict(tile=[128, 192], offset=1, direction="zn")),
         ("C4", dict(tile=[128, 192], offset=1, direction="zn", xcd_remap=1)),
+        ("C4", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, path=3)),
         ("C5", dict(tile=[256, 256], offset=1, direction="zn")),
-        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1)),
-        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, dynamic=1)),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, path=2)),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, path=2, dynamic=1)),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, path=3)),
+        ("C5", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1, path=3, dynamic=1)),
         ("SK", dict(tile=[128, 128], offset=4, direction="zn", xcd_remap=1)),
     ]
     plan = []
@@ -357,7 +360,8 @@ def sweep_configs(args, bst, I, gpu, torch):
         label = "%s %dx%d %s%s" % (name, kw["tile"][0], kw["tile"][1],
                                    "%s%d" % (kw["direction"].capitalize(), kw["offset"]),
                                    "".join(" %s" % k for k in ("xcd_remap", "shuffle_k", "dynamic")
-                                           if kw.get(k)))
+                                           if kw.get(k)) +
+                                   (" path%d" % kw["path"] if kw.get("path") else ""))
         plan.append({"label": label, "workload": wl, "dtype": dt, "flop": flop,
                      "mfma_cycles": flop / MFMA_FLOP_PER_CLK[dt], "alg_bytes": alg, "sched": kw})
     _run_plan(args, plan, runners, torch)
@@ -580,11 +584,13 @@ def all_configs(args, bst, I, gpu, torch):
     Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
     f4 = 2.0 * b["batch"] * b["M"] * b["N"] * b["K"]
     for kw in (dict(tile=(128, 192), offset=1, direction="zn"),
-               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1),
-               dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1)):
+               dict(tile=(128, 192), offset=1, direction="zn", xcd_remap=1),
+               dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2)):
         run("C4 bf16 16x512x768x1024", f4, "bf16", kw, lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s))
-    run("C4 bf16 16x512x768x1024", f4, "bf16", dict(tile=(128, 192), offset=1, direction="zn",
-                                                    xcd_remap=1),
+    # two resident workgroups per CU (the automatic choice at 128x128: 384 tiles)
+    run("C4 bf16 16x512x768x1024", f4, "bf16", dict(tile=(128, 128), offset=4, direction="zn",
+                                                    xcd_remap=1, path=3),
         lambda s: bst.batched_gemm(Ab, Bb, Cb, sched=s), cold=True, clock=True)
     oracle_time(orc, "C4 bf16 16x512x768x1024", 2.0 * b["N"] * b["K"], b["batch"] * b["M"],
                 lambda rows: orc.gemm(orc.BF16, b["A"], b["B"], batch=b["batch"], M=b["M"],
@@ -601,11 +607,14 @@ def all_configs(args, bst, I, gpu, torch):
     for kw in (dict(tile=(256, 256), offset=1, direction="zn"),
                dict(tile=(256, 256), offset=1, direction="zn", xcd_remap=1),
                dict(tile=(256, 128), offset=2, direction="zn", xcd_remap=1),
-               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1),
-               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, preload=1)):
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2, preload=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2, dynamic=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=3)):
         run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8", kw, c5)
+    # two resident workgroups per CU (the automatic choice at 128x128) with dynamic allocation
     run("C5 int8 grouped 8192x4096x2048 dequant", f5, "i8",
-        dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, dynamic=1), c5,
+        dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=3, dynamic=1), c5,
         cold=True, clock=True)
     oracle_time(orc, "C5 int8 grouped 8192x4096x2048 dequant", 2.0 * g["N"] * g["K"],
                 int(g["group_m"].sum()),
@@ -619,6 +628,7 @@ def all_configs(args, bst, I, gpu, torch):
     Ck = torch.empty((k["G"], k["M"], k["N"]), dtype=torch.bfloat16, device="cuda")
     fk = 2.0 * k["M"] * k["N"] * k["total_k"]
     for kw in (dict(tile=(256, 256), offset=1, direction="zn", xcd_remap=1),
+               dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, split_k=2),
                dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)):
         run("int8 grouped slice-K 8 x (1024x2048), K 8192, dequant", fk, "i8", kw,
             lambda s: bst.grouped_gemm_slice_k(Ak, Bk, gk, Ck, row_scale=rk, col_scale=ck, sched=s),
@@ -845,15 +855,22 @@ def phases(args, torch, np, I, gpu):
     Cb = torch.empty((b["batch"], b["M"], b["N"]), dtype=torch.bfloat16, device="cuda")
     sbt = bst.make_sched(tile=(128, 192), offset=1, direction="zn", xcd_remap=1)
     one("C4 bf16 16x512x768x1024 128x192", lambda: bst.batched_gemm(Ab, Bb, Cb, sched=sbt))
+    sb3 = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=3)
+    one("C4 bf16 16x512x768x1024 128x128 two workgroups per CU",
+        lambda: bst.batched_gemm(Ab, Bb, Cb, sched=sb3))
     g = I.workload("int8_groups")
     Ag, Bg, gm = gpu(g["A"], "i8"), gpu(g["B"], "i8"), gpu(g["group_m"], "i32")
     rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
     Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
     for extra in ({}, {"preload": 1}, {"dynamic": 1}):
-        sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, **extra)
+        sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2,
+                            **extra)
         one("C5 int8 grouped 128x128 %s" % (" ".join(extra) or "static"),
             lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs, sched=sg))
-    sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)
+    sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=3)
+    one("C5 int8 grouped 128x128 two workgroups per CU",
+        lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs, sched=sg))
+    sg = bst.make_sched(tile=(128, 128), offset=4, direction="zn", xcd_remap=1, path=2)
     Craw = torch.empty((g["total_m"], g["N"]), dtype=torch.int32, device="cuda")
     one("C5 int8 grouped 128x128 raw int32 (no dequant)",
         lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Craw, sched=sg))
