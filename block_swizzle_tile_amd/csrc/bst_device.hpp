@@ -232,7 +232,10 @@ struct Task {
 // clamped to the rows still left in the allocation (negative sizes count as
 // 0), so the task count never exceeds ceil(total_m / BM) + G tile-rows.
 struct GroupTable {
-  uint32_t first_task[kMaxGroups + 1];
+  union {
+    uint32_t first_task[kMaxGroups + 1];  // slice-M: each group's first task
+    uint32_t order[kMaxGroups + 1];       // slice-K: the groups in run order (below)
+  };
   int64_t first_row[kMaxGroups + 1];
 };
 
@@ -262,8 +265,8 @@ __device__ __forceinline__ void build_group_table(GroupTable& gt, const GemmArgs
 // earlier groups' sizes summed), first_row[G] the end of the last group.
 // Sizes below 0 count as 0 and a group is cut to the K still left of
 // total_k, so no group reads past the allocation.
-__host__ __device__ inline void fill_k_table(GroupTable& gt, const int32_t* group_k, int G,
-                                             int64_t total_k) {
+__host__ __device__ inline void fill_k_prefix(GroupTable& gt, const int32_t* group_k, int G,
+                                              int64_t total_k) {
   int64_t q = 0;
   for (int g = 0; g < G; ++g) {
     gt.first_row[g] = q;
@@ -274,9 +277,48 @@ __host__ __device__ inline void fill_k_table(GroupTable& gt, const int32_t* grou
   gt.first_row[G] = q;
 }
 
+// Run order of slice-K groups: every tile of group g costs in proportion to
+// its K size, so the tasks of the longest groups go first (largest K first,
+// ties by index; the longest-processing-time-first rule) and the short ones
+// fill in behind them instead of ending the launch on a few long tiles.
+// order[r] is the group of rank r.  Ranking is O(G) per group, so beyond
+// kOrderMaxGroups groups the index order is kept.  Only which workgroup runs
+// a task, and when, changes: every task still computes its own tile.
+constexpr int kOrderMaxGroups = 256;
+__host__ __device__ inline void rank_k_group(GroupTable& gt, int G, int i) {
+  if (G > kOrderMaxGroups) {
+    gt.order[i] = (uint32_t)i;
+    return;
+  }
+  const int64_t ki = gt.first_row[i + 1] - gt.first_row[i];
+  int r = 0;
+  for (int j = 0; j < G; ++j) {
+    const int64_t kj = gt.first_row[j + 1] - gt.first_row[j];
+    r += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+  }
+  gt.order[r] = (uint32_t)i;
+}
+
+__host__ inline void fill_k_table(GroupTable& gt, const int32_t* group_k, int G,
+                                  int64_t total_k) {
+  fill_k_prefix(gt, group_k, G, total_k);
+  for (int i = 0; i < G; ++i) rank_k_group(gt, G, i);
+}
+
 __device__ __forceinline__ void build_k_table(GroupTable& gt, const GemmArgs& a) {
-  if (threadIdx.x == 0) fill_k_table(gt, a.group_k, a.G, a.total_k);
+  if (threadIdx.x == 0) fill_k_prefix(gt, a.group_k, a.G, a.total_k);
   __syncthreads();
+  for (int i = (int)threadIdx.x; i < a.G; i += (int)blockDim.x) rank_k_group(gt, a.G, i);
+  __syncthreads();
+}
+
+// Task of position t in the run order of a slice-K launch: the groups'
+// tasks are numbered like batches (t / tiles per group), and the group
+// position maps through the run order.
+__host__ __device__ __forceinline__ uint32_t slicek_task(const GemmArgs& a, const GroupTable* gt,
+                                                         uint32_t t) {
+  const uint32_t pos = a.mc.core.div(t);
+  return gt->order[pos] * a.mc.core.d + (t - pos * a.mc.core.d);
 }
 
 // K range [k0, k1) of slice s of a task whose K runs over [kq, kq + kg):
@@ -475,6 +517,15 @@ __device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
 // ------------------------------------------------------------ epilogue --
 // Shared by both kernel families: the fixed-order split-K fix-up and the
 // conversion / dequant / masked store of a wave's 32x32 sub-tiles.
+// A call the epilogue makes once its dequant scale loads are issued (no-op
+// by default).  The dynamic allocation requests its next ticket there: a
+// device-scope atomic issued before those loads would have to complete
+// before the scales could be used, since vector-memory operations are
+// counted in issue order.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 template <int AB, int BM, int BN, int WM, int WN, int FORM>
 struct Epilogue {
   using T = Traits<AB>;
@@ -636,10 +687,11 @@ struct Epilogue {
   // rows (those partial lines stay dirty in L2 and cost their write-back
   // when the kernel ends).  All waves of the workgroup call this together
   // (it has barriers).
-  template <int OUT, bool DEQ, bool FULL, int SB, bool ADD>
+  template <int OUT, bool DEQ, bool FULL, int SB, bool ADD, class Hook = NoHook>
   __device__ static __forceinline__ void store_as(const GemmArgs& a, const Task& tk,
                                                   const Acc (&acc)[FM][FN], uint32_t wm,
-                                                  uint32_t wn, lds_byte_t* stage) {
+                                                  uint32_t wn, lds_byte_t* stage,
+                                                  const Hook& hook = Hook()) {
     constexpr int OS = (OUT == OUT_F16 || OUT == OUT_BF16) ? 2 : 4;
     constexpr int PITCH = BN * OS + 16;
     constexpr int NTH = 64 * WM * WN;
@@ -691,6 +743,7 @@ struct Epilogue {
             csv[j][g][r] = (FULL || nl + r < tk.nAct) ? csb[nl + r] : 0.0f;
         }
     }
+    hook();
     // One pass: the wave's rows (those of staging pass `pass` when staged).
     auto emit = [&](uint32_t pass) {
 #pragma unroll
@@ -803,18 +856,21 @@ struct Epilogue {
     }
   }
 
-  template <bool DEQ, bool FULL, int SB, bool ADD = false>
+  template <bool DEQ, bool FULL, int SB, bool ADD = false, class Hook = NoHook>
   __device__ static __forceinline__ void store_kind(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
-                                                    uint32_t wn, lds_byte_t* stage) {
+                                                    uint32_t wn, lds_byte_t* stage,
+                                                    const Hook& hook = Hook()) {
     if (a.cdtype == OUT_F16)
-      store_as<OUT_F16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_F16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage, hook);
     else if (a.cdtype == OUT_BF16)
-      store_as<OUT_BF16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_BF16, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage, hook);
     else if (a.cdtype == OUT_F32)
-      store_as<OUT_F32, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_F32, DEQ, FULL, SB, ADD>(a, tk, acc, wm, wn, stage, hook);
     else if constexpr (T::IS_INT && !DEQ)
-      store_as<OUT_I32, false, FULL, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_as<OUT_I32, false, FULL, SB, ADD>(a, tk, acc, wm, wn, stage, hook);
+    else
+      hook();
   }
 
   // matmul-add: the addend's four values at p (of the output kind OUT) are
@@ -873,24 +929,25 @@ struct Epilogue {
   // whole tiles may be staged through (see store_as; SB = 0: none).
   // ADD: the matmul-add instances, whose epilogue adds a.X (never with the
   // dequant, which the host rules out for them).
-  template <int SB = 0, bool ADD = false>
+  template <int SB = 0, bool ADD = false, class Hook = NoHook>
   __device__ static __forceinline__ void store_tile(const GemmArgs& a, const Task& tk,
                                                     const Acc (&acc)[FM][FN], uint32_t wm,
-                                                    uint32_t wn, lds_byte_t* stage = nullptr) {
+                                                    uint32_t wn, lds_byte_t* stage = nullptr,
+                                                    const Hook& hook = Hook()) {
     const bool full = tk.rows_valid >= (uint32_t)BM && tk.nAct >= (uint32_t)BN;
     if constexpr (T::IS_INT && !ADD) {
       if (a.row_scale != nullptr) {
         if (full)
-          store_kind<true, true, SB>(a, tk, acc, wm, wn, stage);
+          store_kind<true, true, SB, false, Hook>(a, tk, acc, wm, wn, stage, hook);
         else
-          store_kind<true, false, SB>(a, tk, acc, wm, wn, stage);
+          store_kind<true, false, SB, false, Hook>(a, tk, acc, wm, wn, stage, hook);
         return;
       }
     }
     if (full)
-      store_kind<false, true, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_kind<false, true, SB, ADD, Hook>(a, tk, acc, wm, wn, stage, hook);
     else
-      store_kind<false, false, SB, ADD>(a, tk, acc, wm, wn, stage);
+      store_kind<false, false, SB, ADD, Hook>(a, tk, acc, wm, wn, stage, hook);
   }
 
 };
@@ -1161,7 +1218,8 @@ struct GemmKernel {
 
     for (uint32_t u = logical_wg(a.remap, a.grid); u < units; u += a.grid) {
       const uint32_t s = u / T_tiles;       // K slice (like GetBatchIdx over slices)
-      const uint32_t t = u - s * T_tiles;   // task
+      uint32_t t = u - s * T_tiles;         // task
+      if constexpr (FORM == FORM_SLICE_K) t = slicek_task(a, gt, t);
       const Task tk = decode_task(a, t, BM, BN, GROUPED ? gt : nullptr);
       // the task's K range: all of K, or its slice-K group's
       uint32_t kq = 0, kg = a.K, ks = a.kslice;

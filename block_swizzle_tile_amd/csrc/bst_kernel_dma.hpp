@@ -757,6 +757,8 @@ struct DmaKernel {
                                                     Ctx& c) {
     un.s = GROUPED ? u / T_tiles : a.mc.tiles.div(u);
     un.t = u - un.s * T_tiles;
+    if constexpr (FORM == FORM_SLICE_K)
+      un.t = __builtin_amdgcn_readfirstlane(slicek_task(a, gt, un.t));
     Task tk = decode_task(a, un.t, BM, BN, GROUPED ? gt : nullptr);
     if constexpr (GROUPED) {
       // the group table lives in LDS: make the task wave-uniform so that
@@ -812,10 +814,14 @@ struct DmaKernel {
   // slow or short-staffed XCD is taken over.  Only the order in which
   // workgroups meet the units changes: each unit computes exactly what it
   // computes under the static stride.  Thread 0 of a workgroup holds its
-  // queue and ticket.  A ticket is requested when a unit's K loop ends, not
-  // before it starts: a wave's vector-memory results return in order, so an
-  // atomic in flight ahead of the stage loads would hold them back, while
-  // after the loop its latency overlaps the fix-up and the epilogue.
+  // queue and ticket.  Vector-memory operations are counted in issue order,
+  // so an atomic in flight holds back every later wait: a ticket requested
+  // before the K loop would delay the stage loads, one requested right after
+  // it the fix-up and the dequant scale loads, and one used right after the
+  // epilogue would wait for its stores.  Tickets are therefore taken one
+  // unit ahead: requested in a unit's epilogue, once the scale loads are out,
+  // and used after the next unit's K loop (by which time it has long
+  // returned) to decide the unit after that.
   //
   // Counter area: one counter per 128-byte line (device-scope atomics on
   // one line are served one at a time): lines 0-7 the queues, line 8 the
@@ -907,6 +913,8 @@ struct DmaKernel {
     const bool dyn = a.queue != nullptr && Q.count > 0;
     const bool preload = !dyn && a.preload != 0;
     uint32_t q = xcc_id(), ticket = 0;  // thread 0's queue and held ticket
+    bool held = false;                  // thread 0: a ticket was requested ahead
+    uint32_t decided = kNoUnit;         // thread 0: the unit after the current one
     // thread 0 publishes the next unit here, alternating slots, so that a
     // slot is rewritten only after a later barrier that every wave passed
     // after reading it
@@ -936,9 +944,18 @@ struct DmaKernel {
           kloop<false>(acc, c, padded_stages(un.nk), wm, wn, a.trace, pre);
       }
       const uint64_t t_epi = trace_stamp();
-      if (dyn && threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+      // dynamic allocation: the unit after this one comes from the ticket
+      // requested during the previous unit's epilogue, complete by now (this
+      // unit's K loop waited for every load issued after it); the first
+      // unit's ticket is requested here
+      if (dyn && threadIdx.x == 0) {
+        if (!held)
+          ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        decided = take(a, Q, q, ticket);
+        next_unit[round & 1u] = decided;
+        held = false;
+      }
       const bool last = Epi::fixup(a, acc, un.s, un.t);
       const uint64_t t_fix = trace_stamp();
       // static stride: the next unit is known now, and with preload its
@@ -960,11 +977,23 @@ struct DmaKernel {
           pre = true;
         }
       }
+      // dynamic allocation: the ticket for the unit after the next is
+      // requested once the epilogue's scale loads are out (its latency then
+      // overlaps the stores and the next K loop), or here when this slice
+      // stores nothing; none once the queues are spent
+      auto request = [&]() {
+        if (dyn && threadIdx.x == 0 && decided != kNoUnit) {
+          ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+          held = true;
+        }
+      };
       if (last)
         Epi::template store_tile<STAGE_BYTES, ADD>(a, un.tk, acc, wm, wn,
-                                                   stage_buf<STAGES - 1, STAGE_BYTES>());
+                                                   stage_buf<STAGES - 1, STAGE_BYTES>(), request);
+      else
+        request();
       if (dyn) {
-        if (threadIdx.x == 0) next_unit[round & 1u] = take(a, Q, q, ticket);
         __syncthreads();
         nu = __builtin_amdgcn_readfirstlane(next_unit[round & 1u]);
         ++round;

@@ -17,6 +17,8 @@
 #include <string>
 #include <vector>
 
+#include <algorithm>
+
 #include "bst_kernel_dma.hpp"
 
 using namespace bst;
@@ -319,6 +321,37 @@ void run_slicek(const std::vector<Problem>& ps) {
   for (const Problem& p : ps) check<AB, BM, BN, WM, WN, S, FORM_SLICE_K>(p);
 }
 
+// The slice-K run order: a permutation of the groups, longest K first, ties
+// by index (checked against a stable sort); the index order beyond the
+// ranking limit; the task mapping a bijection of each launch's tasks.
+static void check_k_order() {
+  const std::vector<std::vector<int32_t>> cases = {
+      {336, 208, 32, 80, 16, 5072, 912, 1536}, {0, 0, 48}, {64, 5, 200, 16, 64, 64},
+      {1}, {-3, 7, 7, 0, 7}, std::vector<int32_t>(300, 16)};
+  for (const auto& gk : cases) {
+    const int G = (int)gk.size();
+    int64_t total = 0;
+    for (int32_t k : gk) total += k > 0 ? k : 0;
+    GroupTable gt;
+    fill_k_table(gt, gk.data(), G, total);
+    std::vector<int> want(G);
+    for (int i = 0; i < G; ++i) want[i] = i;
+    if (G <= kOrderMaxGroups)
+      std::stable_sort(want.begin(), want.end(), [&](int x, int y) {
+        return (gt.first_row[x + 1] - gt.first_row[x]) > (gt.first_row[y + 1] - gt.first_row[y]);
+      });
+    for (int r = 0; r < G; ++r)
+      REQUIRE((int)gt.order[r] == want[r], "k order G=%d rank %d: %u, want %d", G, r,
+              gt.order[r], want[r]);
+    GemmArgs a{};
+    a.mc.core = make_fastdiv(6);  // 6 tiles per group
+    std::vector<int> seen(6 * G, 0);
+    for (uint32_t t = 0; t < 6u * G; ++t) ++seen[slicek_task(a, &gt, t)];
+    for (int t = 0; t < 6 * G; ++t) REQUIRE(seen[t] == 1, "k order task %d seen %d times", t, seen[t]);
+    ++g_checked;
+  }
+}
+
 // The division by invariant integers against the hardware-free '/': every
 // divisor up to 4096 and a spread of larger ones, each with the dividends
 // that sit at and around its multiples and at the ends of the range.
@@ -365,6 +398,7 @@ static void check_fast_map() {
 int main() {
   check_fastdiv();
   check_fast_map();
+  check_k_order();
   // 16-bit operands: K and N multiples of 8 elements
   const std::vector<Problem> p16 = {
       plain("tails", 200, 136, 256, 0, 0, 1),      plain("tails-split", 200, 136, 256, 8, 16, 3),
