@@ -11,6 +11,8 @@ static const Instance kList[] = {
     BST_DMA(AB_MXE4M3, 256, 128, 2, 2, 3, FORM_DENSE), BST_DMA(AB_MXE4M3, 256, 256, 4, 2, 2, FORM_DENSE),
     BST_DMA(AB_MXE4M3, 128, 64, 2, 2, 4, FORM_DENSE),  BST_DMA(AB_MXE4M3, 64, 128, 2, 2, 4, FORM_DENSE),
     BST_DMA_ADD(AB_MXE4M3, 64, 128, 2, 2, 4), BST_DMA_ADD(AB_MXE4M3, 128, 128, 2, 2, 4),
+    // two resident workgroups per CU, two stages
+    BST_DMA_PAIR(AB_MXE4M3, 128, 128, 2, 2, 2, FORM_DENSE),
 };
 
 InstanceList instances_mxfp8() { return InstanceList{kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }

@@ -87,7 +87,8 @@ typedef struct bst_sched {
                                   two resident workgroups per CU and two stages, so that one
                                   workgroup's epilogue and set-up overlap the other's K loop
                                   (fp16 / bf16 / int8 at 128x128, plain, batched and grouped
-                                  slice-M; BST_E_UNSUPPORTED otherwise); 0 = automatic: path 1
+                                  slice-M; MX-fp8 at 128x128, plain; BST_E_UNSUPPORTED
+                                  otherwise); 0 = automatic: path 1
                                   when the layout rules out the LDS-DMA family, else path 3
                                   where it exists and the launch has more work units than CUs,
                                   else path 2.  Paths 2 and 3 add the same products in the

@@ -482,6 +482,7 @@ int main() {
   run_plain<AB_E4M3, 128, 64, 2, 2, 4>(p8);
   run_plain<AB_E4M3, 64, 128, 2, 2, 4>(p8);
   run_plain<AB_MXE4M3, 128, 128, 2, 2, 4>(pmx);
+  run_plain<AB_MXE4M3, 128, 128, 2, 2, 2>(pmx);
   run_plain<AB_MXE4M3, 256, 128, 2, 2, 3>(pmx);
   run_plain<AB_MXE4M3, 256, 256, 4, 2, 2>(pmx);
   if (g_fail) {

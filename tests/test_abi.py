@@ -143,12 +143,14 @@ def test_two_workgroup_family_selection(L):
     assert eff(0, _lib.BF16, 16, 512, 768, 1024, tile=(128, 128)) == (_lib.OK, 3)
     # a split that brings the units above the CU count
     assert eff(0, _lib.F16, 1, 1024, 1024, 2048, tile=(128, 128), split_k=8) == (_lib.OK, 3)
-    # no such instance: other tiles, slice-K, MX, matmul-add
+    # no such instance: other tiles, slice-K, plain e4m3, matmul-add
     assert eff(0, _lib.F16, 1, 4096, 4096, 256, tile=(64, 64), path=3)[0] == _lib.E_UNSUPPORTED
     assert eff(0, _lib.F16, 1, 4096, 4096, 256, tile=(64, 64)) == (_lib.OK, 2)
     assert eff(3, _lib.I8, 8, 1024, 2048, 8192, tile=(128, 128), path=3)[0] == _lib.E_UNSUPPORTED
     assert eff(3, _lib.I8, 8, 1024, 2048, 8192, tile=(128, 128)) == (_lib.OK, 2)
-    assert eff(0, _lib.MXE4M3, 1, 4096, 4096, 256, tile=(128, 128)) == (_lib.OK, 2)
+    assert eff(0, _lib.MXE4M3, 1, 4096, 4096, 256, tile=(128, 128)) == (_lib.OK, 3)
+    assert eff(0, _lib.MXE4M3, 1, 4096, 4096, 256, tile=(64, 128)) == (_lib.OK, 2)
+    assert eff(0, _lib.E4M3, 1, 4096, 4096, 256, tile=(128, 128), path=3)[0] == _lib.E_UNSUPPORTED
     # a layout the LDS-DMA family cannot take: the register-staged family, and path 3 refused
     assert eff(0, _lib.F16, 1, 4096, 4096, 250, tile=(128, 128)) == (_lib.OK, 1)
     assert eff(0, _lib.F16, 1, 4096, 4096, 250, tile=(128, 128), path=3)[0] == _lib.E_UNSUPPORTED

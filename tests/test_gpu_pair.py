@@ -184,3 +184,26 @@ def test_16bit_batched_and_grouped(orc, kind):
     assert np.array_equal(codes(G3), codes(G2))
     check_close(orc, G3, refg, deng, TOL_16, "16-bit groups")
     torch.cuda.synchronize()
+
+
+def test_mxfp8_pair(orc):
+    """MX-fp8 at 128x128 with two workgroups per CU: ragged M / N with K tails of whole 128-wide
+    blocks, several units per workgroup, a split; bit-identical to path 2, within 2^-7."""
+    import torch
+    from gpu_util import TOL_8
+    M, N, K = 300, 272, 640
+    g = I.rng(87, 0)
+    sa = (127 + g.integers(-2, 3, size=(M, K // 32))).astype(np.uint8)
+    sb = (127 + g.integers(-2, 3, size=(K // 32, N))).astype(np.uint8)
+    A = I.e4m3_bits(g.standard_normal((M, K)) * 4.0)
+    B = I.e4m3_bits(g.standard_normal((K, N)) * 4.0)
+    ref, den = orc.gemm(orc.MXE4M3, A, B, scale_a=sa, scale_b=sb, tile=(128, 128))
+    At, Bt = to_gpu(A, "e4m3"), to_gpu(B, "e4m3")
+    sat, sbt = to_gpu(sa, "u8"), to_gpu(sb, "u8")
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    for base in [dict(tile=(128, 128)), dict(tile=(128, 128), grid=2, xcd_remap=1),
+                 dict(tile=(128, 128), split_k=2), dict(tile=(128, 128), grid=3, dynamic=1)]:
+        C3, C2 = _pair_and_single(lambda s: bst().gemm(At, Bt, scale_a=sat, scale_b=sbt, sched=s,
+                                                       workspace=ws), base, "mx")
+        check_close(orc, C3, ref, den, TOL_8, str(base))
+        assert np.array_equal(codes(C3), codes(C2)), base
