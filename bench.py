@@ -883,7 +883,7 @@ def phases(args, torch, np, I, gpu):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the GEMM would shard by tiles / batches / groups with no exchange)",
               file=sys.stderr)
         sys.exit(2)

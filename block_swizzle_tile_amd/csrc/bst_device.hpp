@@ -517,11 +517,11 @@ __device__ __forceinline__ u32x4_t load16(const uint8_t* p, int valid) {
 // ------------------------------------------------------------ epilogue --
 // Shared by both kernel families: the fixed-order split-K fix-up and the
 // conversion / dequant / masked store of a wave's 32x32 sub-tiles.
-// A call the epilogue makes once its dequant scale loads are issued (no-op
-// by default).  The dynamic allocation requests its next ticket there: a
-// device-scope atomic issued before those loads would have to complete
-// before the scales could be used, since vector-memory operations are
-// counted in issue order.
+// A call the epilogue makes before its first store: after its dequant scale
+// loads are issued where it gathers them up front (no-op by default).  The
+// dynamic allocation requests its next ticket there: a device-scope atomic
+// issued before those loads would have to complete before the scales could
+// be used, since vector-memory operations are counted in issue order.
 struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
