@@ -140,6 +140,9 @@ def parse():
     p.add_argument("--phases", action="store_true",
                    help="with the cycle-accounting build (python -m block_swizzle_tile_amd.build "
                         "--trace): where a work unit's cycles go, per workload")
+    p.add_argument("--wg-times", action="store_true",
+                   help="per-workgroup start / end times of one launch of C5 and the slice-K "
+                        "workload per schedule, from the production kernels' clock record")
     p.add_argument("--sweep-configs", action="store_true",
                    help="launch every configuration's named and fastest schedules --steps times "
                         "each, eagerly and in a fixed order, for per-dispatch rocprofv3 counters")
@@ -880,6 +883,67 @@ def phases(args, torch, np, I, gpu):
         one("fp16 8192x8192x4096 256x256", lambda: bst.gemm(Al, Bl, Cl, sched=sl, **kw), waves=8)
 
 
+def wg_times(args, torch, np, I, gpu):
+    """Per-workgroup life of one launch (after 0.1 s of warm-up launches), from the production
+    kernels' clock record (bst_set_clock_record: the 100 MHz reference counter at each
+    workgroup's start and end): the spread of the end times, their maximum per XCD (workgroup w
+    runs on XCD w mod 8), and the time by which all but the last 1% / 10% had ended.  One JSON
+    line per (workload, schedule).  It shows how evenly a schedule spreads the units."""
+    import block_swizzle_tile_amd as bst
+
+    def one(name, kind, ab, count, M, N, K, sk, fn):
+        s = bst.make_sched(**sk)
+        eff = bst.effective_sched(kind, ab, count, M, N, K, s)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            fn(s)
+            torch.cuda.synchronize()
+        nwg = 1024
+        buf = torch.zeros(4 * nwg, dtype=torch.int64, device="cuda")
+        bst.clock_record(buf, nwg)
+        try:
+            fn(s)
+            torch.cuda.synchronize()
+        finally:
+            bst.clock_record()
+        t = buf.cpu().view(nwg, 4).numpy()
+        idx = np.nonzero(t[:, 3] == 1)[0]
+        st, en = t[idx, 0].astype(np.float64), t[idx, 1].astype(np.float64)
+        base = st.min()
+        st, en = (st - base) / 100.0, (en - base) / 100.0   # microseconds
+        rec = {"workload": name, "sched": {k: list(v) if isinstance(v, tuple) else v
+                                           for k, v in sk.items()},
+               "path": eff.path, "workgroups": int(len(idx)),
+               "last_start_us": round(float(st.max()), 2),
+               "end_us": {"min": round(float(en.min()), 2), "median": round(float(np.median(en)), 2),
+                          "p90": round(float(np.percentile(en, 90)), 2),
+                          "p99": round(float(np.percentile(en, 99)), 2),
+                          "max": round(float(en.max()), 2)},
+               "end_max_by_xcd_us": [round(float(en[idx % 8 == x].max()), 1) for x in range(8)]}
+        print(json.dumps(rec), flush=True)
+
+    g = I.workload("int8_groups")
+    Ag, Bg, gm = gpu(g["A"], "i8"), gpu(g["B"], "i8"), gpu(g["group_m"], "i32")
+    rs, cs = gpu(g["row_scale"], "f32"), gpu(g["col_scale"], "f32")
+    Cg = torch.empty((g["total_m"], g["N"]), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    c5 = lambda s: bst.grouped_gemm_slice_m(Ag, Bg, gm, Cg, row_scale=rs, col_scale=cs, sched=s,
+                                            workspace=ws)
+    base = dict(tile=(128, 128), offset=4, direction="zn", xcd_remap=1)
+    for extra in (dict(path=2), dict(path=2, dynamic=1), dict(path=3), dict(path=3, dynamic=1)):
+        one("C5 int8 grouped 8192x4096x2048 dequant", 1, bst.I8, g["G"], g["total_m"], g["N"],
+            g["K"], dict(base, **extra), c5)
+    k = I.workload("int8_slice_k")
+    Ak, Bk, gk = gpu(k["A"], "i8"), gpu(k["B"], "i8"), gpu(k["group_k"], "i32")
+    rk, ck = gpu(k["row_scale"], "f32"), gpu(k["col_scale"], "f32")
+    Ck = torch.empty((k["G"], k["M"], k["N"]), dtype=torch.bfloat16, device="cuda")
+    sk = lambda s: bst.grouped_gemm_slice_k(Ak, Bk, gk, Ck, row_scale=rk, col_scale=ck, sched=s,
+                                            workspace=ws)
+    for extra in ({}, dict(dynamic=1), dict(xcd_remap=0)):
+        one("int8 grouped slice-K 8 x (1024x2048), K 8192, dequant", 3, bst.I8, k["G"], k["M"],
+            k["N"], k["total_k"], dict(base, **extra), sk)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -920,6 +984,9 @@ def main():
 
     if args.clock:
         clock(args, torch, np, I, gpu)
+        return
+    if args.wg_times:
+        wg_times(args, torch, np, I, gpu)
         return
     if args.phases:
         phases(args, torch, np, I, gpu)

@@ -35,7 +35,7 @@ def test_modes_are_documented_in_help():
     assert r.returncode == 0
     for flag in ("--all-configs", "--l2-sweep", "--large", "--clock", "--calib-copy",
                  "--traffic-from", "--shuffle-k", "--mx-shuffle-k", "--sweep-configs",
-                 "--plan-out", "--summarize"):
+                 "--plan-out", "--summarize", "--phases", "--wg-times"):
         assert flag in r.stdout, flag
 
 
