@@ -395,6 +395,30 @@ static void check_fast_map() {
         }
 }
 
+// Random plain problems of the shape class the GPU tests draw at random:
+// M in [1, 320), N and K whole 16-byte chunks up to a few hundred (MX: K in
+// blocks of 128), splits 1-3; a fixed xorshift seed.
+static std::vector<Problem> random_plain(int n, int q, int kq, bool scaled, uint64_t seed) {
+  std::vector<Problem> v;
+  uint64_t x = seed;
+  auto next = [&]() {
+    x ^= x << 13;
+    x ^= x >> 7;
+    x ^= x << 17;
+    return x;
+  };
+  static char names[64][16];
+  for (int i = 0; i < n && i < 64; ++i) {
+    const int64_t M = 1 + (int64_t)(next() % 319);
+    const int64_t N = q * (1 + (int64_t)(next() % (320 / q)));
+    const int64_t K = kq * (1 + (int64_t)(next() % 19));
+    const uint32_t split = 1 + (uint32_t)(next() % 3);
+    snprintf(names[i], sizeof(names[i]), "rnd%d", i);
+    v.push_back(plain(names[i], M, N, K, 0, 0, split, 1, scaled));
+  }
+  return v;
+}
+
 int main() {
   check_fastdiv();
   check_fast_map();
@@ -485,6 +509,33 @@ int main() {
   run_plain<AB_MXE4M3, 128, 128, 2, 2, 2>(pmx);
   run_plain<AB_MXE4M3, 256, 128, 2, 2, 3>(pmx);
   run_plain<AB_MXE4M3, 256, 256, 4, 2, 2>(pmx);
+  // random shapes on every plain instance of both operand widths and the MX one
+  const std::vector<Problem> r16 = random_plain(24, 8, 8, false, 0x9E3779B97F4A7C15ull);
+  const std::vector<Problem> r8 = random_plain(24, 16, 16, false, 0xD1B54A32D192ED03ull);
+  const std::vector<Problem> rmx = random_plain(16, 16, 128, true, 0x8CB92BA72F3D8DD7ull);
+  run_plain<AB_F16, 64, 64, 2, 2, 4>(r16);
+  run_plain<AB_F16, 128, 128, 2, 2, 4>(r16);
+  run_plain<AB_F16, 128, 128, 2, 2, 2>(r16);
+  run_plain<AB_F16, 256, 128, 2, 2, 3>(r16);
+  run_plain<AB_F16, 128, 256, 2, 2, 3>(r16);
+  run_plain<AB_F16, 128, 192, 2, 2, 3>(r16);
+  run_plain<AB_F16, 128, 64, 2, 2, 4>(r16);
+  run_plain<AB_F16, 64, 128, 2, 2, 4>(r16);
+  run_plain<AB_F16, 256, 256, 4, 2, 2>(r16);
+  run_plain<AB_I8, 64, 64, 2, 2, 4>(r8);
+  run_plain<AB_I8, 128, 128, 2, 2, 4>(r8);
+  run_plain<AB_I8, 128, 128, 2, 2, 2>(r8);
+  run_plain<AB_I8, 256, 128, 2, 2, 3>(r8);
+  run_plain<AB_I8, 256, 256, 4, 2, 2>(r8);
+  run_plain<AB_E4M3, 128, 64, 2, 2, 4>(r8);
+  run_plain<AB_E4M3, 64, 128, 2, 2, 4>(r8);
+  run_plain<AB_MXE4M3, 64, 64, 2, 2, 4>(rmx);
+  run_plain<AB_MXE4M3, 128, 128, 2, 2, 4>(rmx);
+  run_plain<AB_MXE4M3, 128, 128, 2, 2, 2>(rmx);
+  run_plain<AB_MXE4M3, 256, 128, 2, 2, 3>(rmx);
+  run_plain<AB_MXE4M3, 256, 256, 4, 2, 2>(rmx);
+  run_plain<AB_MXE4M3, 128, 64, 2, 2, 4>(rmx);
+  run_plain<AB_MXE4M3, 64, 128, 2, 2, 4>(rmx);
   if (g_fail) {
     printf("FAILED: %d violations (%lld accesses checked)\n", g_fail, g_checked);
     return 1;
