@@ -279,8 +279,8 @@ __host__ __device__ inline void fill_k_prefix(GroupTable& gt, const int32_t* gro
 
 // Run order of slice-K groups: every tile of group g costs in proportion to
 // its K size, so the tasks of the longest groups go first (largest K first,
-// ties by index; the longest-processing-time-first rule) and the short ones
-// fill in behind them instead of ending the launch on a few long tiles.
+// ties by index; the longest-processing-time-first rule): they start in the
+// first round, and the short ones fill in behind them.
 // order[r] is the group of rank r.  Ranking is O(G) per group, so beyond
 // kOrderMaxGroups groups the index order is kept.  Only which workgroup runs
 // a task, and when, changes: every task still computes its own tile.
