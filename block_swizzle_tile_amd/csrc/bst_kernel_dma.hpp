@@ -126,6 +126,30 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_range<0, N>(f);
 }
 
+// The kernel's argument block, read in place in the kernarg segment (the
+// kernels take GemmArgs as their only argument, so it starts there).  Each
+// call yields a new pointer, so the loads through it are issued after this
+// point: a phase of the kernel (a unit's set-up, its epilogue) loads the
+// fields it uses there, together, instead of the compiler loading every
+// field at the kernel's start and keeping (spilling) the values across the
+// K loop.  The cast back to a generic pointer keeps the constant address
+// space visible to the compiler, so the loads stay scalar.
+__device__ __forceinline__ const GemmArgs* kernel_args() {
+  auto p = (const __attribute__((address_space(4))) GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return (const GemmArgs*)p;
+}
+
+// Brings every 64-byte line of the argument block into the scalar cache in
+// one round trip (one word of each, combined into an empty asm operand), so
+// that the set-up's dependent reads of the arguments hit in it.
+__device__ __forceinline__ void warm_args(const GemmArgs* ap) {
+  static_assert(sizeof(GemmArgs) <= 6 * 64, "the argument block spans at most six lines");
+  const uint32_t* w = (const uint32_t*)ap;
+  const uint32_t x = w[0] ^ w[16] ^ w[32] ^ w[48] ^ w[64] ^ w[80];
+  asm volatile("" ::"s"(x));
+}
+
 // Shader-clock stamp for the BST_TRACE cycle accounting (0 otherwise).
 __device__ __forceinline__ uint64_t trace_stamp() {
 #ifdef BST_TRACE
@@ -880,38 +904,45 @@ struct DmaKernel {
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  __device__ __attribute__((always_inline)) static void run(const GemmArgs& a) {
+  // Grouped slice-M kernels keep the compiler's own argument handling (all
+  // loaded at the start): reading them per phase raised their vector
+  // register use past the budget of the two-workgroup and 256x256 builds.
+  static constexpr bool kPhaseArgs = FORM != FORM_SLICE_M;
+
+  __device__ __attribute__((always_inline)) static void run(const GemmArgs& a0) {
+    const GemmArgs* ap = kPhaseArgs ? kernel_args() : &a0;
     uint64_t t_start = trace_stamp();
+    if constexpr (kPhaseArgs) warm_args(ap);
     ClockMark clk;
-    clk.start(a);
+    clk.start(*ap);
 #ifdef BST_TRACE
     const uint64_t clk_ref0 = __builtin_amdgcn_s_memrealtime();
     const uint64_t clk_sh0 = t_start;
 #endif
     GroupTable* gt = nullptr;
-    uint32_t T_tiles = a.tiles;
+    uint32_t T_tiles = ap->tiles;
     if constexpr (FORM != FORM_DENSE) {
       __shared__ GroupTable gtab;
       gt = &gtab;
       if constexpr (FORM == FORM_SLICE_M) {
-        build_group_table(gtab, a, BM, (a.N + BN - 1) / BN);
-        T_tiles = gtab.first_task[a.G];
+        build_group_table(gtab, *ap, BM, (ap->N + BN - 1) / BN);
+        T_tiles = gtab.first_task[ap->G];
       } else {
-        build_k_table(gtab, a);
+        build_k_table(gtab, *ap);
       }
     }
-    const uint32_t units = T_tiles * a.split;
+    const uint32_t units = T_tiles * ap->split;
     Ctx c;
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    c.ldb_bytes = a.ldb * ES;
-    c.ldsb = a.ldsb;
+    c.ldb_bytes = ap->ldb * ES;
+    c.ldsb = ap->ldsb;
     c.ldb_bytes32 = (uint32_t)c.ldb_bytes;
-    c.ldsb32 = (uint32_t)a.ldsb;
+    c.ldsb32 = (uint32_t)ap->ldsb;
     const uint32_t wm = c.wave / WN, wn = c.wave % WN;
     // dynamic allocation, when there are units past the first round
-    const Queues Q{a.grid, units > a.grid ? units - a.grid : 0u};
-    const bool dyn = a.queue != nullptr && Q.count > 0;
-    const bool preload = !dyn && a.preload != 0;
+    const Queues Q{ap->grid, units > ap->grid ? units - ap->grid : 0u};
+    const bool dyn = ap->queue != nullptr && Q.count > 0;
+    const bool preload = !dyn && ap->preload != 0;
     uint32_t q = xcc_id(), ticket = 0;  // thread 0's queue and held ticket
     bool held = false;                  // thread 0: a ticket was requested ahead
     uint32_t decided = kNoUnit;         // thread 0: the unit after the current one
@@ -923,11 +954,11 @@ struct DmaKernel {
 
     // The host launches at most one workgroup per unit, so a plain launch's
     // first unit exists (a grouped launch learns its unit count here).
-    uint32_t u = logical_wg(a.remap, a.grid);
+    uint32_t u = logical_wg(ap->remap, ap->grid);
     bool have = !GROUPED || u < units;
     bool pre = false;  // the unit's first stages were issued ahead
     Unit un;
-    if (have) setup_unit(a, gt, T_tiles, u, un, c);
+    if (have) setup_unit(*ap, gt, T_tiles, u, un, c);
     while (have) {
       const uint64_t t_loop = trace_stamp();
       Acc acc[FM][FN];
@@ -939,36 +970,37 @@ struct DmaKernel {
           for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
       if (un.nk > 0) {
         if (un.whole)
-          kloop<true>(acc, c, padded_stages(un.nk), wm, wn, a.trace, pre);
+          kloop<true>(acc, c, padded_stages(un.nk), wm, wn, ap->trace, pre);
         else
-          kloop<false>(acc, c, padded_stages(un.nk), wm, wn, a.trace, pre);
+          kloop<false>(acc, c, padded_stages(un.nk), wm, wn, ap->trace, pre);
       }
       const uint64_t t_epi = trace_stamp();
+      if constexpr (kPhaseArgs) ap = kernel_args();
       // dynamic allocation: the unit after this one comes from the ticket
       // requested during the previous unit's epilogue, complete by now (this
       // unit's K loop waited for every load issued after it); the first
       // unit's ticket is requested here
       if (dyn && threadIdx.x == 0) {
         if (!held)
-          ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+          ticket = __hip_atomic_fetch_add(&ap->queue[q * kLine], 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
-        decided = take(a, Q, q, ticket);
+        decided = take(*ap, Q, q, ticket);
         next_unit[round & 1u] = decided;
         held = false;
       }
-      const bool last = Epi::fixup(a, acc, un.s, un.t);
+      const bool last = Epi::fixup(*ap, acc, un.s, un.t);
       const uint64_t t_fix = trace_stamp();
       // static stride: the next unit is known now, and with preload its
       // first stage goes out before this unit's epilogue, whose staging
       // uses a buffer the stage does not.  Only the unit index is kept across
       // the epilogue (its set-up is redone after it), so that the
       // epilogue's registers stay its own.
-      uint32_t nu = dyn ? kNoUnit : u + a.grid;
+      uint32_t nu = dyn ? kNoUnit : u + ap->grid;
       pre = false;
       if (preload && nu < units) {
         Unit nx;
         Ctx cn = c;
-        setup_unit(a, gt, T_tiles, nu, nx, cn);
+        setup_unit(*ap, gt, T_tiles, nu, nx, cn);
         if (nx.nk > 0) {
           if (nx.whole)
             preload_stage0<true>(cn);
@@ -983,13 +1015,13 @@ struct DmaKernel {
       // stores nothing; none once the queues are spent
       auto request = [&]() {
         if (dyn && threadIdx.x == 0 && decided != kNoUnit) {
-          ticket = __hip_atomic_fetch_add(&a.queue[q * kLine], 1u, __ATOMIC_RELAXED,
+          ticket = __hip_atomic_fetch_add(&ap->queue[q * kLine], 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
           held = true;
         }
       };
       if (last)
-        Epi::template store_tile<STAGE_BYTES, ADD>(a, un.tk, acc, wm, wn,
+        Epi::template store_tile<STAGE_BYTES, ADD>(*ap, un.tk, acc, wm, wn,
                                                    stage_buf<STAGES - 1, STAGE_BYTES>(), request);
       else
         request();
@@ -1004,13 +1036,13 @@ struct DmaKernel {
         const uint64_t t_end = trace_stamp();
         __builtin_amdgcn_s_waitcnt(0);
         const uint64_t t_done = trace_stamp();
-        if (a.trace != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
-          uint64_t* o = a.trace + 32 + (threadIdx.x >> 6) * 4;
+        if (ap->trace != nullptr && blockIdx.x == 0 && (threadIdx.x & 63u) == 0) {
+          uint64_t* o = ap->trace + 32 + (threadIdx.x >> 6) * 4;
           o[0] += t_loop - t_start;  // unit set-up (first unit: from kernel start)
           o[1] += t_epi - t_loop;    // K loop
           o[2] += t_end - t_epi;     // fix-up, preload, epilogue, next ticket
           o[3] += 1;                 // units
-          uint64_t* r = a.trace + 64 + (threadIdx.x >> 6) * 4;
+          uint64_t* r = ap->trace + 64 + (threadIdx.x >> 6) * 4;
           r[0] += t_fix - t_epi;     // fix-up
           r[1] += t_end - t_fix;     // preload, stores issued, next ticket
           r[2] += t_done - t_end;    // stores complete
@@ -1022,23 +1054,23 @@ struct DmaKernel {
       (void)t_fix;
 #endif
       if (have) {
-        setup_unit(a, gt, T_tiles, nu, un, c);
+        setup_unit(*ap, gt, T_tiles, nu, un, c);
         u = nu;
       }
       t_start = trace_stamp();
     }
-    if (dyn && threadIdx.x == 0) queue_exit(a);
-    clk.stop(a);
+    if (dyn && threadIdx.x == 0) queue_exit(*ap);
+    clk.stop(*ap);
 #ifdef BST_TRACE
     // Clock record of the first 256 workgroups at trace[128 + 4 w]: the
     // 100 MHz reference counter at the start and at the end, and the shader
     // cycles in between, so shader cycles / reference ticks gives the shader
     // clock the workgroup ran at.
-    if (a.trace != nullptr && threadIdx.x == 0 && blockIdx.x < 256) {
+    if (ap->trace != nullptr && threadIdx.x == 0 && blockIdx.x < 256) {
       __builtin_amdgcn_s_waitcnt(0);
       const uint64_t sh1 = __builtin_amdgcn_s_memtime();
       const uint64_t ref1 = __builtin_amdgcn_s_memrealtime();
-      uint64_t* o = a.trace + 128 + 4 * blockIdx.x;
+      uint64_t* o = ap->trace + 128 + 4 * blockIdx.x;
       o[0] = clk_ref0;
       o[1] = ref1;
       o[2] = sh1 - clk_sh0;
