@@ -877,10 +877,11 @@ def phases(args, torch, np, I, gpu):
     Craw = torch.empty((g["total_m"], g["N"]), dtype=torch.int32, device="cuda")
     one("C5 int8 grouped 128x128 raw int32 (no dequant)",
         lambda: bst.grouped_gemm_slice_m(Ag, Bg, gm, Craw, sched=sg))
-    for i, (wl, M, N, K) in enumerate(LARGE_SHAPES[1:2]):
+    for wl, M, N, K in LARGE_SHAPES[1::2]:
         Al, Bl, Cl, kw = large_operands(torch, wl, M, N, K, 1001)
         sl = bst.make_sched(tile=(256, 256), offset=4, direction="zn", xcd_remap=1)
-        one("fp16 8192x8192x4096 256x256", lambda: bst.gemm(Al, Bl, Cl, sched=sl, **kw), waves=8)
+        one("%s %dx%dx%d 256x256" % ("fp16" if wl == "f16" else "MX-fp8", M, N, K),
+            lambda: bst.gemm(Al, Bl, Cl, sched=sl, **kw), waves=8)
 
 
 def wg_times(args, torch, np, I, gpu):
