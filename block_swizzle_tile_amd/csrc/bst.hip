@@ -147,6 +147,7 @@ struct Layout {
   int64_t lda = 0, ldb = 0;
   const void* sa = nullptr;
   const void* sb = nullptr;
+  int64_t ldc_bytes = 0;  // C's row pitch in bytes (0: not known, the query calls)
 };
 
 bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, const Layout& L) {
@@ -156,6 +157,8 @@ bool dma_fits(bst_dtype ab, int64_t N, int64_t K, uint32_t bm, uint32_t bk, cons
   // stage's scalar offset (K position) stay below 2^31
   if ((int64_t)bm * L.lda * es + K * es >= (1LL << 31)) return false;
   if ((K + bk) * L.ldb * es >= (1LL << 31)) return false;
+  // the staged epilogue addresses a C tile with 31-bit offsets too
+  if ((int64_t)bm * L.ldc_bytes >= (1LL << 31)) return false;
   if (ab == BST_MXE4M3 && (K / 32 + 4) * N >= (1LL << 31)) return false;  // B scales [K/32][N]
   if (ab == BST_MXE4M3 && (K % 128 != 0 || ((uintptr_t)L.sa & 3u) || ((uintptr_t)L.sb & 3u)))
     return false;
@@ -376,7 +379,7 @@ bst_status prepare_dense(bst_dtype ab, bst_dtype c, int64_t batch, int64_t M, in
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
                  (batch > 1 && (!stride_ok(strideA, es) || !stride_ok(strideB, es))))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
-  const Layout lay{lda, ldb, sa, sb};
+  const Layout lay{lda, ldb, sa, sb, ldc * (int64_t)ec};
   st = make_plan(FORM_DENSE, ab, batch, M, N, K, s, true, p, &lay, X != nullptr);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
@@ -638,7 +641,7 @@ bst_status bst_gemm_padded(bst_dtype ab, bst_dtype c, int64_t M, int64_t N, int6
   bst_status st = make_plan(FORM_DENSE, ab, 1, M, N, K, s, false, p);
   if (st != BST_OK) return st;
   const Padded q = padded_layout(ab, M, N, K);
-  const Layout lay{q.lda, q.ldb, scale_a, scale_b};
+  const Layout lay{q.lda, q.ldb, scale_a, scale_b, ldc * (int64_t)elem_size(c)};
   st = make_plan(FORM_DENSE, ab, 1, M, N, q.kp, s, true, p, &lay);
   if (st != BST_OK) return st;
   // The GEMM's own workspace comes first, its split-K counters at offset 0
@@ -715,7 +718,7 @@ bst_status bst_grouped_gemm_slice_m(bst_dtype ab, bst_dtype c, int32_t G, const 
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es) ||
                  !stride_ok(strideB, es))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
-  const Layout lay{lda, ldb, nullptr, nullptr};
+  const Layout lay{lda, ldb, nullptr, nullptr, ldc * (int64_t)ec};
   st = make_plan(FORM_SLICE_M, ab, G, total_m, N, K, s, true, p, &lay);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);
@@ -773,7 +776,7 @@ bst_status bst_grouped_gemm_slice_k(bst_dtype ab, bst_dtype c, int32_t G, const 
   if (!aligned16(C) || !stride_ok(ldc, ec) || (G > 1 && !stride_ok(strideC, ec)) ||
       (has_k && (!aligned16(A) || !aligned16(B) || !stride_ok(lda, es) || !stride_ok(ldb, es))))
     return fail(BST_E_ALIGN, "pointers and strides must be 16-byte multiples");
-  const Layout lay{lda, ldb, nullptr, nullptr};
+  const Layout lay{lda, ldb, nullptr, nullptr, ldc * (int64_t)ec};
   st = make_plan(FORM_SLICE_K, ab, G, M, N, total_k, s, true, p, &lay);
   if (st != BST_OK) return st;
   st = check_ws(p, ws, ws_bytes);

@@ -837,9 +837,8 @@ struct Epilogue {
       // The tile goes through the L2 to memory (device-scope cache policy):
       // its lines do not stay dirty in the XCD's L2, where they would take
       // the place of A and B panel lines and wait to be written back when
-      // the kernel ends.  The buffer offsets are 32-bit, so a tile whose
-      // rows span 2 GiB or more is stored with plain stores.
-      const bool through = (uint64_t)BM * (uint64_t)a.ldc * OS < 0x80000000ull;
+      // the kernel ends.  The buffer offsets are 31-bit: the host runs
+      // these kernels only where a tile's rows of C span less than 2 GiB.
       const __amdgpu_buffer_rsrc_t crsrc =
           __builtin_amdgcn_make_buffer_rsrc(cbase, (short)0, (int)0x7fffffff, 0x00020000);
       // a loop, not unrolled: each wave writes in the passes that hold its
@@ -853,12 +852,8 @@ struct Epilogue {
           const uint32_t q = fresh_v(threadIdx.x) + (uint32_t)i * NTH;
           const uint32_t row = q / CPR, c = q % CPR;
           const u32x4_t v = *(const lds_u32x4_out_t*)(stage + row * PITCH + c * 16);
-          if (through)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                v, crsrc, (pass * RP + row) * (uint32_t)a.ldc * OS + c * 16, 0, kDeviceScope);
-          else
-            *(u32x4_t*)__builtin_assume_aligned(
-                cbase + (int64_t)(pass * RP + row) * a.ldc * OS + c * 16, 16) = v;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, crsrc, (pass * RP + row) * (uint32_t)a.ldc * OS + c * 16, 0, kDeviceScope);
         }
         // the next pass (or the next task's prologue) refills the buffer
         __syncthreads();

@@ -83,7 +83,8 @@ typedef struct bst_sched {
   uint32_t path;               /* kernel family: 1 = register-staged (any shape);
                                   2 = LDS-DMA pipeline, one workgroup per CU with a deep
                                   pipeline (K and N whole 16-byte chunks, MX K a multiple of
-                                  128; BST_E_UNSUPPORTED otherwise); 3 = LDS-DMA pipeline with
+                                  128, and a tile's rows of A, B and C each within 2 GiB;
+                                  BST_E_UNSUPPORTED otherwise); 3 = LDS-DMA pipeline with
                                   two resident workgroups per CU and two stages, so that one
                                   workgroup's epilogue and set-up overlap the other's K loop
                                   (fp16 / bf16 / int8 at 128x128, plain, batched and grouped

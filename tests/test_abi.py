@@ -79,6 +79,16 @@ def test_validation_errors(L):
     assert b"swizzle_offset" in gemm_msg(L, sched=S(offset=0))
 
 
+def test_lds_dma_family_needs_c_tiles_within_2gib(L):
+    """The LDS-DMA kernels store a C tile with 31-bit offsets: a row pitch that makes one tile's
+    rows span 2 GiB or more rules them out (path 2 refused before any launch); the register-staged
+    family takes it."""
+    big = (1 << 31) // (64 * 2)          # fp16 elements: 64 rows of this pitch are exactly 2 GiB
+    assert gemm(L, ldc=big, sched=S(tile=(64, 64), path=2)) == _lib.E_UNSUPPORTED
+    assert b"LDS-DMA" in L.bst_last_error()
+    assert gemm(L, ldc=big - 8, sched=S(tile=(64, 64), path=2)) != _lib.E_UNSUPPORTED
+
+
 def gemm_msg(L, **kw):
     gemm(L, **kw)
     return L.bst_last_error()
