@@ -54,6 +54,14 @@ __device__ __forceinline__ lds_t* stage_buf() {
   return (lds_t*)buf;
 }
 
+// The ring of A-scale groups (see DmaKernel::SAG): an LDS array of its
+// own, apart from the stage buffers.
+template <int BYTES>
+__device__ __forceinline__ lds_t* sag_buf() {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[BYTES];
+  return (lds_t*)buf;
+}
+
 // Buffer descriptor over [base, base + 2^31): raw (stride 0) 32-bit data.
 __device__ __forceinline__ u32x4_t make_desc(const uint8_t* base) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
@@ -230,20 +238,41 @@ struct DmaKernel {
   static constexpr int B_BYTES = BK * RB;
   static constexpr int A_IPW = A_BYTES / 1024 / NW;  // 1 KiB DMA instructions per wave
   static constexpr int B_IPW = B_BYTES / 1024 / NW;
+  static constexpr int UNR = STAGES;  // steps per loop trip: buffer index stays compile-time
+  // A's scales in whole tasks (SAG).  A row's scales lie in one line of
+  // memory, 4 bytes per stage, so per-stage loads read a line per row for 4
+  // useful bytes.  In four-stage kernels (a trip of four steps holds one
+  // group of four stages, so a group starts at a fixed step), whole tasks
+  // starting on a group boundary load them a group at a time instead: 16
+  // bytes per row (dword-by-4 DMA, 64 rows per instruction) at the group's
+  // first stage, into one of two group slots ([row][16 bytes], group g in
+  // slot g mod 2); at the group's other stages the A slots load nothing and
+  // write zeros to their places in the stage, which these tasks do not
+  // read.  The instruction count per stage stays the same.
+  static constexpr bool SAG = T::SCALED && STAGES == 4;
+  static constexpr int SAG_SLOT = SAG ? BM * 16 : 0;
+  static constexpr uint32_t SAG_DUMMY = 2u * SAG_SLOT;  // a dummy kilobyte
+  static constexpr int SAG_BYTES = SAG ? 2 * SAG_SLOT + 1024 : 16;
   // MX scales: A as [BM rows][4 bytes] (one dword = the stage's 4 K blocks
   // of a row), B as [4][BN] bytes; dword DMA, 256 bytes per instruction:
   // SA_N instructions for A (64 rows each) and SB_N for B.  They are dealt
-  // out as slots, SC_IPW per wave (wave w takes slots w*SC_IPW + i), so a
-  // wave issues at most one more than its share; a slot past SA_N + SB_N
-  // issues an all-out-of-range instruction (it writes zeros) into the
-  // stage's 256-byte dummy area, so that every wave issues the same count
-  // for the vmcnt arithmetic.
+  // out as slots, SC_IPW per wave: with A-scale groups A's and B's apart
+  // (SCA_IPW A slots per wave, wave w taking A instructions w*SCA_IPW + i,
+  // then SCB_IPW B slots), so that a slot's matrix, and with it the
+  // instruction form, is fixed at compile time; otherwise together (wave w
+  // takes slots w*SC_IPW + i of A's, then B's), which needs fewer slots.  A
+  // slot past its instructions issues an all-out-of-range instruction (it
+  // writes zeros) into the stage's 256-byte dummy area, so that every wave
+  // issues the same count for the vmcnt arithmetic.
   static constexpr int SA_N = T::SCALED ? BM / 64 : 0;
   static constexpr int SB_N = T::SCALED ? BN / 64 : 0;
-  static constexpr int SC_IPW = (SA_N + SB_N + NW - 1) / NW;
+  static constexpr int SCA_IPW = SAG ? (SA_N + NW - 1) / NW : 0;
+  static constexpr int SCB_IPW = SAG ? (SB_N + NW - 1) / NW : 0;
+  static constexpr int SC_IPW = SAG ? SCA_IPW + SCB_IPW : (SA_N + SB_N + NW - 1) / NW;
   static constexpr int SA_BYTES = SA_N * 256;
   static constexpr int SB_BYTES = SB_N * 256;
-  static constexpr int SD_BYTES = SC_IPW * NW > SA_N + SB_N ? 256 : 0;
+  static constexpr int SD_BYTES = (SAG ? (SCA_IPW * NW > SA_N || SCB_IPW * NW > SB_N)
+                                       : SC_IPW * NW > SA_N + SB_N) ? 256 : 0;
   static constexpr int LPS = A_IPW + B_IPW + SC_IPW;  // DMA instructions / wave / stage
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SD_BYTES;
 
@@ -252,9 +281,12 @@ struct DmaKernel {
   static_assert(!T::SCALED || (BM % 64 == 0 && BN % 64 == 0), "whole 256-byte scale instructions");
   static_assert(LPS * STAGES < 64, "vmcnt holds 6 bits");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 MFMA sub-tiles");
-  static_assert(STAGES * STAGE_BYTES <=
+  static_assert(STAGES * STAGE_BYTES + (SAG ? SAG_BYTES : 0) <=
                     160 * 1024 - (FORM != FORM_DENSE ? (int)sizeof(GroupTable) : 0) - 16,
                 "LDS budget");
+  // a group slot is rewritten STAGES-1 stages ahead of its group; the group
+  // two back must be done with by then
+  static_assert(!SAG || STAGES <= 5, "A-scale groups need at most five stages");
 
   static __host__ __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
     if constexpr (ES == 2)
@@ -368,12 +400,31 @@ struct DmaKernel {
     uint32_t idx, lds;
   };
   __host__ __device__ __forceinline__ static ScSlot sc_slot(uint32_t wave, int i) {
-    const uint32_t x = wave * SC_IPW + (uint32_t)i;
-    if (x < (uint32_t)SA_N) return ScSlot{0, x, A_BYTES + B_BYTES + x * 256u};
-    if (x < (uint32_t)(SA_N + SB_N))
-      return ScSlot{1, x - SA_N, A_BYTES + B_BYTES + SA_BYTES + (x - SA_N) * 256u};
-    return ScSlot{2, 0u, (uint32_t)(A_BYTES + B_BYTES + SA_BYTES + SB_BYTES)};
+    constexpr uint32_t dummy = (uint32_t)(A_BYTES + B_BYTES + SA_BYTES + SB_BYTES);
+    if (!SAG) {
+      const uint32_t x = wave * SC_IPW + (uint32_t)i;
+      if (x < (uint32_t)SA_N) return ScSlot{0, x, A_BYTES + B_BYTES + x * 256u};
+      if (x < (uint32_t)(SA_N + SB_N))
+        return ScSlot{1, x - SA_N, A_BYTES + B_BYTES + SA_BYTES + (x - SA_N) * 256u};
+      return ScSlot{2, 0u, dummy};
+    }
+    if (i < SCA_IPW) {  // an A slot
+      const uint32_t x = wave * SCA_IPW + (uint32_t)i;
+      return x < (uint32_t)SA_N ? ScSlot{0, x, A_BYTES + B_BYTES + x * 256u} : ScSlot{2, 0u, dummy};
+    }
+    const uint32_t y = wave * SCB_IPW + (uint32_t)(i - SCA_IPW);
+    return y < (uint32_t)SB_N ? ScSlot{1, y, A_BYTES + B_BYTES + SA_BYTES + y * 256u}
+                              : ScSlot{2, 0u, dummy};
   }
+  // A-scale groups: group slot of the task's stage j, the byte offset in the
+  // ring at which the MFMA operand reads find stage j's dword of row 0 (row
+  // r: + 16 r), and the LDS offset of A scale instruction idx (rows 64 idx
+  // ..) inside a group slot.  Host-callable for the CPU check.
+  __host__ __device__ __forceinline__ static uint32_t sag_slot(uint32_t j) { return (j >> 2) & 1u; }
+  __host__ __device__ __forceinline__ static uint32_t sag_read(uint32_t j) {
+    return sag_slot(j) * SAG_SLOT + (j & 3u) * 4u;
+  }
+  __host__ __device__ __forceinline__ static uint32_t sag_lds(uint32_t idx) { return idx * 1024u; }
 
   // Per-task DMA state: buffer descriptors over the task's panels and, for
   // a task whose every stage lies inside its K slice (no partial and no
@@ -387,6 +438,7 @@ struct DmaKernel {
     u32x4_t rsc[SC_IPW > 0 ? SC_IPW : 1];   // scale slot i: its matrix's descriptor,
     uint32_t sclds[SC_IPW > 0 ? SC_IPW : 1];  // its byte offset inside a stage,
     uint32_t scb;                             // bit i: slot i reads B's scales
+    uint32_t sag[2][SCA_IPW > 0 ? SCA_IPW : 1];  // A slot i: its group destination per slot
     uint32_t vo[LPS];
   };
 
@@ -417,6 +469,12 @@ struct DmaKernel {
         d.rsc[i] = sl.kind == 1 ? rsb : rsa;
         d.sclds[i] = sl.lds;
         if (sl.kind == 1) d.scb |= 1u << i;
+        if (i < SCA_IPW) {
+          // a padding A slot loads its (all out-of-range) group into the
+          // dummy kilobyte
+          d.sag[0][i] = sl.kind == 0 ? sag_lds(sl.idx) : SAG_DUMMY;
+          d.sag[1][i] = sl.kind == 0 ? SAG_SLOT + sag_lds(sl.idx) : SAG_DUMMY;
+        }
       }
     }
     if constexpr (FULL) {
@@ -429,6 +487,7 @@ struct DmaKernel {
   // Scalar byte offsets of the stage at K index kb0 inside each panel.
   struct Soff {
     uint32_t kb0, a, b, sa, sb;
+    uint32_t gslot;  // A-scale groups: the stage's group slot
   };
   // K index of the task's stage j.  With ShuffleK (whole-stage tasks only)
   // the stages start at kshift and wrap around; otherwise nks = ~0 and the
@@ -439,12 +498,20 @@ struct DmaKernel {
   }
 
   __device__ static __forceinline__ Soff stage_soff(const Ctx& c, uint32_t kb0) {
-    return Soff{kb0, kb0 * (uint32_t)ES, kb0 * c.ldb_bytes32, kb0 / 32u, (kb0 / 32u) * c.ldsb32};
+    return Soff{kb0, kb0 * (uint32_t)ES, kb0 * c.ldb_bytes32, kb0 / 32u, (kb0 / 32u) * c.ldsb32,
+                0u};
+  }
+  // The offsets of the task's stage j.
+  __device__ static __forceinline__ Soff stage_so(const Ctx& c, uint32_t j) {
+    Soff so = stage_soff(c, stage_k(c, j));
+    so.gslot = sag_slot(j);
+    return so;
   }
 
   // DMA instruction X (0 <= X < LPS) of this wave for the stage of `so`,
-  // into stage buffer S.
-  template <int S, int X, bool FULL>
+  // into stage buffer S.  GST: whole tasks with A-scale groups, the stage
+  // starts a group.
+  template <int S, int X, bool FULL, bool GST>
   __device__ static __forceinline__ void dma_one(const Ctx& c, const Dma& d, const Soff& so) {
     lds_t* base = stage_buf<S, STAGE_BYTES>();
     if constexpr (X < A_IPW) {
@@ -455,19 +522,31 @@ struct DmaKernel {
       const uint32_t v = FULL ? d.vo[X] : b_access(c.ln, i, so.kb0, c.kend).voff;
       dma16(d.rb, base + b_lds(c.wave, i), v, so.b);
     } else {
-      // a scale slot: the selects are wave-uniform, so they stay scalar and
-      // add no branch to the step
+      // a scale slot: which matrix is fixed by the slot index, a padding slot
+      // differs only in its offsets, so no branch enters the step
       constexpr int i = X - A_IPW - B_IPW;
       const uint32_t v = FULL ? d.vo[X] : sc_access(c.ln, i, so.kb0, c.kend).voff;
-      dma4(d.rsc[i], base + d.sclds[i], v, ((d.scb >> i) & 1u) ? so.sb : so.sa);
+      if constexpr (!SAG) {
+        dma4(d.rsc[i], base + d.sclds[i], v, ((d.scb >> i) & 1u) ? so.sb : so.sa);
+      } else if constexpr (i >= SCA_IPW) {
+        dma4(d.rsc[i], base + d.sclds[i], v, so.sb);
+      } else if constexpr (!FULL) {
+        dma4(d.rsc[i], base + d.sclds[i], v, so.sa);
+      } else if constexpr (GST) {
+        // the group's 16 bytes of each row, from its first scale
+        dma16(d.rsc[i], sag_buf<SAG_BYTES>() + (so.gslot ? d.sag[1][i] : d.sag[0][i]), v,
+              so.sa & ~15u);
+      } else {
+        dma4(d.rsc[i], base + d.sclds[i], kOob, 0u);
+      }
     }
   }
 
-  // Enqueue the whole DMA of the stage at K index kb0 into stage buffer S.
-  template <int S, bool FULL>
-  __device__ static __forceinline__ void issue(const Ctx& c, const Dma& d, uint32_t kb0) {
-    const Soff so = stage_soff(c, kb0);
-    static_for<LPS>([&](auto x) { dma_one<S, decltype(x)::value, FULL>(c, d, so); });
+  // Enqueue the whole DMA of the task's stage j into stage buffer S.
+  template <int S, bool FULL, bool GST>
+  __device__ static __forceinline__ void issue(const Ctx& c, const Dma& d, uint32_t j) {
+    const Soff so = stage_so(c, j);
+    static_for<LPS>([&](auto x) { dma_one<S, decltype(x)::value, FULL, GST>(c, d, so); });
   }
 
   // MFMA operands of one K step of a wave, held in registers.
@@ -480,8 +559,10 @@ struct DmaKernel {
 
   // LDS -> registers, one operand fragment at a time: A fragment I and B
   // fragment J of K step KK of stage buffer S, with their block scales.
-  template <int S, int KK, int I>
-  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm) {
+  // sar: whole tasks with A-scale groups, the stage's read offset in the
+  // group ring (sag_read).
+  template <int S, int KK, int I, bool FULL>
+  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, uint32_t sar) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
     const lds_t* lsa = base + A_BYTES + B_BYTES;
@@ -497,10 +578,14 @@ struct DmaKernel {
       f.a[I] = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
                        (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
     }
-    if constexpr (T::SCALED)
+    if constexpr (SAG && FULL)
+      f.sa[I] = (*(const lds_u32_t*)(sag_buf<SAG_BYTES>() + sar + row * 16) >> (8 * (2 * KK + hi))) &
+                0xffu;
+    else if constexpr (T::SCALED)
       f.sa[I] = (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * KK + hi))) & 0xffu;
     else
       f.sa[I] = 0x7fu;  // 2^0 (the scale operand only matters to fp8 MFMAs)
+    (void)sar;
   }
 
   template <int S, int KK, int J>
@@ -553,16 +638,18 @@ struct DmaKernel {
   static constexpr int NMK = FM * FN;       // MFMAs per K step
   static constexpr int NMF = KSTEPS * NMK;  // MFMAs per stage
 
-  template <int S, int KK, int X>
-  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn) {
+  template <int S, int KK, int X, bool FULL>
+  __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn,
+                                                 uint32_t sar) {
     if constexpr (X < FM)
-      load_a<S, KK, X>(f, wm);
+      load_a<S, KK, X, FULL>(f, wm, sar);
     else
       load_b<S, KK, X - FM>(f, wn);
   }
-  template <int S, int KK>
-  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn) {
-    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value>(f, wm, wn); });
+  template <int S, int KK, bool FULL>
+  __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn,
+                                                   uint32_t sar) {
+    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value, FULL>(f, wm, wn, sar); });
   }
 
   // MFMA Q of a K step (A fragment major).
@@ -579,11 +666,11 @@ struct DmaKernel {
   // NMF slots; with 2 the stage in flight has only the current stage's
   // compute to land in, so its instructions go one per slot from the first.
   static constexpr int DSLOTS = (STAGES == 2 && LPS < NMF) ? LPS : NMF;
-  template <int SD, int Q, bool FULL>
+  template <int SD, int Q, bool FULL, bool GST>
   __device__ static __forceinline__ void slot_dma(const Ctx& c, const Dma& d, const Soff& so) {
     if constexpr (Q < DSLOTS)
       static_for_range<(Q * LPS) / DSLOTS, ((Q + 1) * LPS) / DSLOTS>(
-          [&](auto x) { dma_one<SD, decltype(x)::value, FULL>(c, d, so); });
+          [&](auto x) { dma_one<SD, decltype(x)::value, FULL, GST>(c, d, so); });
   }
 
   template <int N>
@@ -606,8 +693,7 @@ struct DmaKernel {
   // K-step (2 stages): the next stage is still in flight during a step, so
   // the reads run inside the stage only: the MFMAs of K step kk carry the
   // reads of K step kk+1.
-  static constexpr int UNR = STAGES;  // steps per loop trip: buffer index stays compile-time
-  static constexpr int RING_K = UNR * KSTEPS;  // K steps per loop trip
+  static constexpr int RING_K = UNR * KSTEPS;  // K steps per loop trip (ring schedule)
   // The ring's read-ahead: as far as 3 K steps (and never past the next
   // stage), with a set count that divides the K steps of one trip so that
   // every set index is a compile-time constant, and with the accumulators
@@ -650,18 +736,24 @@ struct DmaKernel {
       barrier_lds();
     }
     tr.released();
-    const Soff so = stage_soff(c, stage_k(c, kt + STAGES - 1));
+    const Soff so = stage_so(c, kt + STAGES - 1);
+    // whole tasks with A-scale groups: the stage issued here starts a group
+    // at a fixed step of the trip; the reads of this stage and the next
+    constexpr bool GST = SAG && FULL && (I + STAGES - 1) % 4 == 0;
+    const uint32_t sar0 = (SAG && FULL) ? sag_read(kt) : 0u;
+    const uint32_t sar1 = (SAG && FULL) ? sag_read(kt + 1) : 0u;
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
       constexpr int G = I * KSTEPS + KK;  // K step inside the trip
       mfma_one<R>(acc, f[G % NSET]);
-      if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
+      if constexpr (DMA) slot_dma<SD, Q, FULL, GST>(c, d, so);
       constexpr int GL = G + PD;  // the K step whose operands are read now
       if constexpr (!(LAST && GL >= RING_K)) {
         constexpr int SB = (GL / KSTEPS) % STAGES, KL = GL % KSTEPS;
+        constexpr bool NEXT = GL / KSTEPS > I;  // the read lies in stage kt+1
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<SB, KL, decltype(x)::value>(f[GL % NSET], wm, wn);
+          load_one<SB, KL, decltype(x)::value, FULL>(f[GL % NSET], wm, wn, NEXT ? sar1 : sar0);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -678,17 +770,19 @@ struct DmaKernel {
     wait_vm<WAITN>();
     barrier_lds();
     tr.released();
-    const Soff so = stage_soff(c, stage_k(c, kt + STAGES - 1));
+    const Soff so = stage_so(c, kt + STAGES - 1);
+    constexpr bool GST = SAG && FULL && (I + STAGES - 1) % 4 == 0;
+    const uint32_t sar = (SAG && FULL) ? sag_read(kt) : 0u;
     KFrag g0, g1;
-    load_kstep<S, 0>(g0, wm, wn);
+    load_kstep<S, 0, FULL>(g0, wm, wn, sar);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
       mfma_one<R>(acc, (KK & 1) ? g1 : g0);
-      if constexpr (DMA) slot_dma<SD, Q, FULL>(c, d, so);
+      if constexpr (DMA) slot_dma<SD, Q, FULL, GST>(c, d, so);
       if constexpr (KK + 1 < KSTEPS) {
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<S, KK + 1, decltype(x)::value>((KK & 1) ? g0 : g1, wm, wn);
+          load_one<S, KK + 1, decltype(x)::value, FULL>((KK & 1) ? g0 : g1, wm, wn, sar);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -701,7 +795,7 @@ struct DmaKernel {
   template <bool FULL>
   __device__ static __forceinline__ void preload_stage0(const Ctx& c) {
     const Dma d = make_dma<FULL>(c);
-    issue<0, FULL>(c, d, stage_k(c, 0));
+    issue<0, FULL, SAG && FULL>(c, d, 0u);
   }
 
   // The K loop of one task: nkp (padded, >= UNR) stages from K index c.k0.
@@ -719,17 +813,17 @@ struct DmaKernel {
     uint32_t kt = 0;
     if constexpr (STAGES > 2) {
       // stages 0..STAGES-2 in flight, then stage 0 resident
-      if (!pre) issue<0, FULL>(c, d, stage_k(c, 0));
+      if (!pre) issue<0, FULL, SAG && FULL>(c, d, 0u);
       static_for_range<1, STAGES - 1>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        issue<I, FULL>(c, d, stage_k(c, I));
+        issue<I, FULL, SAG && FULL && I % 4 == 0>(c, d, (uint32_t)I);
       });
       wait_vm<(STAGES - 2) * LPS>();
       barrier_lds();
       KFrag f[NSET];
       static_for<PD>([&](auto g) {
         constexpr int GG = decltype(g)::value;
-        load_kstep<0, GG>(f[GG], wm, wn);
+        load_kstep<0, GG, FULL>(f[GG], wm, wn, (SAG && FULL) ? sag_read(0u) : 0u);
       });
       tr.prologue_done();
       // At the top of step kt the stages up to kt+STAGES-2 have been
@@ -750,15 +844,20 @@ struct DmaKernel {
         step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr);
       });
     } else {
-      if (!pre) issue<0, FULL>(c, d, stage_k(c, 0));
+      if (!pre) issue<0, FULL, SAG && FULL>(c, d, 0u);
       tr.prologue_done();
-      for (; kt + STAGES < nkp; kt += STAGES) {
-        step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
-        step_kstep<1, FULL, true, 0>(acc, c, d, kt + 1, wm, wn, tr);
+      constexpr int U = STAGES;
+      for (; kt + U < nkp; kt += U) {
+        static_for<U>([&](auto i) {
+          constexpr int I = decltype(i)::value;
+          step_kstep<I, FULL, true, 0>(acc, c, d, kt + I, wm, wn, tr);
+        });
       }
-      // last group: only its first step has a stage left to issue
-      step_kstep<0, FULL, true, 0>(acc, c, d, kt, wm, wn, tr);
-      step_kstep<1, FULL, false, 0>(acc, c, d, kt + 1, wm, wn, tr);
+      // last trip: every step but the last has a stage left to issue
+      static_for<U>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        step_kstep<I, FULL, I + 1 < U, 0>(acc, c, d, kt + I, wm, wn, tr);
+      });
     }
     // every wave is done with the stage buffers before the next task's
     // prologue refills them
@@ -819,10 +918,14 @@ struct DmaKernel {
     c.sb_tile = T::SCALED ? a.sb + (int64_t)tk.n * BN : nullptr;
     c.k0 = k0;
     c.kend = k1;
-    un.whole = un.nk > 0 && full_task(k0, k1);
-    // ShuffleK: tasks of the launch's full stage count S start at stage t mod S
+    // kernels with A-scale groups run whole tasks only from a group
+    // boundary (their stage count is a whole number of groups already)
+    un.whole = un.nk > 0 && full_task(k0, k1) && (!SAG || (k0 / BK) % 4u == 0u);
+    // ShuffleK: tasks of the launch's full stage count S start at stage t mod
+    // S (with A-scale groups: rounded down to a group boundary)
     const bool shuffle = a.shuffle_k != 0 && un.whole && un.nk == a.mc.nk_full.d;
     c.kshift = shuffle ? un.t - a.mc.nk_full.div(un.t) * un.nk : 0u;
+    if constexpr (SAG) c.kshift &= ~3u;
     c.nks = shuffle ? un.nk : 0xFFFFFFFFu;
     lane_setup(c.ln, c.wave, fresh_v(threadIdx.x & 63u), tk.rows_valid, tk.n, a.N, a.lda,
                c.ldb_bytes, a.ldsa, a.ldsb);

@@ -8,7 +8,11 @@
 //   1. every enabled global access (16 bytes of A or B, 4 bytes of a scale
 //      block) lies inside the valid rows and columns of its matrix;
 //   2. every LDS destination lies inside the stage buffer;
-//   3. each stage loads every valid chunk of the tile exactly once.
+//   3. each stage loads every valid chunk of the tile exactly once;
+//   4. where whole MX tasks load A's scales a group of four stages at a time
+//      (DmaKernel::SAG), every group load reads 16 bytes inside its row,
+//      lands in its group slot, every stage's scale read finds its own
+//      group there, and no slot is rewritten while a stage still reads it.
 // Prints "ALL OK" and exits 0, or prints the first violation and exits 1.
 // Build: hipcc --cuda-host-only -std=c++17 -I include -I <csrc> check_dma_bounds.hip
 #include <cstdio>
@@ -131,6 +135,13 @@ void check(const Problem& p) {
       // offsets: they must equal the checked ones at every stage
       const bool full = nk > 0 && KN::full_task(k0, k1);
       auto same = [](uint32_t u, uint32_t v) { return u == v || (u >= kOob && v >= kOob); };
+      // whole MX tasks starting on a group boundary load A's scales by groups
+      if constexpr (KN::SAG) {
+        if (p.scaled && full && (k0 / BK) % 4 == 0) {
+          REQUIRE(nk % 4 == 0, "grouped task of %u stages", nk);
+          check_scale_groups<KN, BM, STAGES>(p, tk, k0, nk, a);
+        }
+      }
       // padding stages (past nk, up to the unroll) must access nothing
       for (uint32_t kt = 0; kt < KN::padded_stages(nk); ++kt) {
         const uint32_t kb0 = k0 + kt * BK;
@@ -262,6 +273,83 @@ void check(const Problem& p) {
             for (int c = 0; c < BN; ++c)
               REQUIRE(covSB[e * BN + c] == (tk.n * BN + c < a.N && kb0 < k1 ? 1 : 0), "SB coverage");
         }
+      }
+    }
+  }
+}
+
+// Whole MX tasks with A-scale groups: for the ShuffleK shifts given, walk
+// the task's stages in issue order, check every group load's addresses, and
+// replay the loads and the operand reads on a timeline of loop steps: a load
+// goes out in the step that issues its stage (j - (S - 1); the stages of the
+// prologue before any read), a stage is read in its own step and, with the
+// ring schedule, the step before.  A read must find its group as the slot's
+// last load from an earlier step, and no load may hit a slot in a step that
+// reads it.
+template <class KN, int BM, int S>
+void check_scale_groups(const Problem& p, const Task& tk, uint32_t k0, uint32_t nk,
+                        const GemmArgs& a) {
+  constexpr int BK = KN::BK;
+  const int64_t row_lo = tk.row0, row_hi = tk.row0 + tk.rows_valid;
+  std::vector<uint32_t> shifts = {0u};
+  if (nk >= 8) shifts.push_back(4u);
+  if (nk >= 4) shifts.push_back(nk - 4);
+  struct Load { int64_t t; uint32_t slot; int64_t group; };
+  for (uint32_t kshift : shifts) {
+    std::vector<Load> loads;
+    for (uint32_t j = 0; j < nk; ++j) {
+      if (j % 4 != 0) continue;
+      const uint32_t kb0 = k0 + ((j + kshift) % nk) * BK;
+      const uint32_t slot = KN::sag_slot(j);
+      REQUIRE(kb0 / 32 % 16 == 0, "group start stage %u not on a 16-scale boundary", j);
+      for (uint32_t w = 0; w < (uint32_t)KN::NW; ++w)
+        for (uint32_t lane = 0; lane < 64; ++lane) {
+          typename KN::Lanes ln;
+          KN::lane_setup(ln, w, lane, tk.rows_valid, tk.n, a.N, a.lda, 0, a.ldsa, a.ldsb);
+          for (int i = 0; i < KN::SCA_IPW; ++i) {
+            const auto sl = KN::sc_slot(w, i);
+            const uint32_t v = KN::full_voff(ln, KN::A_IPW + KN::B_IPW + i);
+            ++g_checked;
+            if (sl.kind != 0) {  // a padding A slot: nothing read, zeros into the dummy kilobyte
+              REQUIRE(sl.kind == 2 && v >= kOob, "padding A slot reads memory");
+              continue;
+            }
+            const uint32_t lds = slot * KN::SAG_SLOT + KN::sag_lds(sl.idx) + lane * 16;
+            const uint32_t r = sl.idx * 64 + lane;  // row inside the tile
+            REQUIRE(lds + 16 <= 2u * KN::SAG_SLOT && lds == slot * KN::SAG_SLOT + r * 16,
+                    "group row %u at lds %u", r, lds);
+            if (v >= kOob) {
+              REQUIRE(r >= tk.rows_valid, "valid row %u without its group", r);
+              continue;
+            }
+            const int64_t addr = tk.row0 * a.ldsa + (int64_t)v + (kb0 / 32);
+            const int64_t R = addr / a.ldsa, c = addr % a.ldsa;
+            REQUIRE(R >= row_lo && R < row_hi && R - tk.row0 == (int64_t)r,
+                    "%s group row %lld outside [%lld,%lld)", p.name.c_str(), (long long)R,
+                    (long long)row_lo, (long long)row_hi);
+            REQUIRE(c == kb0 / 32 && c + 16 <= a.ldsa, "%s group col %lld (ldsa %lld)",
+                    p.name.c_str(), (long long)c, (long long)a.ldsa);
+          }
+        }
+      const int64_t t = j < (uint32_t)(S - 1) ? -2 : (int64_t)j - (S - 1);
+      loads.push_back(Load{t, slot, (int64_t)(kb0 / 32 / 16)});
+    }
+    for (uint32_t j = 0; j < nk; ++j) {
+      const uint32_t kidx = (j + kshift) % nk, kb0 = k0 + kidx * BK;
+      const uint32_t slot = KN::sag_slot(j), sar = KN::sag_read(j);
+      REQUIRE(sar == slot * KN::SAG_SLOT + (kidx % 4) * 4, "stage %u reads offset %u", j, sar);
+      for (int64_t tr = (S >= 3 ? (int64_t)j - 1 : (int64_t)j); tr <= (int64_t)j; ++tr) {
+        const Load* last = nullptr;
+        for (const Load& l : loads) {
+          if (l.slot != slot) continue;
+          REQUIRE(l.t != tr, "slot %u loaded in step %lld, which reads stage %u", slot,
+                  (long long)tr, j);
+          if (l.t < tr && (!last || l.t > last->t)) last = &l;
+        }
+        ++g_checked;
+        REQUIRE(last && last->group == (int64_t)(kb0 / 32 / 16),
+                "%s stage %u (step %lld) finds group %lld in slot %u, wants %u", p.name.c_str(), j,
+                (long long)tr, last ? (long long)last->group : -1LL, slot, kb0 / 32 / 16);
       }
     }
   }
@@ -494,7 +582,9 @@ int main() {
   const std::vector<Problem> pmx = {plain("mx", 256, 512, 1024, 0, 0, 1, 1, true),
                                     plain("mxtail", 200, 144, 384, 128, 16, 2, 1, true),
                                     plain("mxsplit", 130, 96, 1024, 0, 0, 3, 1, true),
-                                    plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true)};
+                                    plain("mx4k", 1024, 2048, 4096, 0, 0, 2, 1, true),
+                                    plain("mx2k3", 200, 256, 2048, 0, 0, 3, 1, true),
+                                    plain("mx2k4", 72, 128, 2048, 0, 0, 4, 1, true)};
   run_plain<AB_MXE4M3, 64, 64, 2, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 128, 64, 2, 2, 4>(pmx);
   run_plain<AB_MXE4M3, 64, 128, 2, 2, 4>(pmx);
