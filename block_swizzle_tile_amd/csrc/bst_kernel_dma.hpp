@@ -416,14 +416,14 @@ struct DmaKernel {
     return y < (uint32_t)SB_N ? ScSlot{1, y, A_BYTES + B_BYTES + SA_BYTES + y * 256u}
                               : ScSlot{2, 0u, dummy};
   }
-  // A-scale groups: group slot of the task's stage j, the byte offset in the
-  // ring at which the MFMA operand reads find stage j's dword of row 0 (row
-  // r: + 16 r), and the LDS offset of A scale instruction idx (rows 64 idx
-  // ..) inside a group slot.  Host-callable for the CPU check.
+  // A-scale groups: group slot of the task's stage j, and the LDS offset of
+  // A scale instruction idx (rows 64 idx ..) inside a group slot.
+  // Host-callable for the CPU check.
   __host__ __device__ __forceinline__ static uint32_t sag_slot(uint32_t j) { return (j >> 2) & 1u; }
-  __host__ __device__ __forceinline__ static uint32_t sag_read(uint32_t j) {
-    return sag_slot(j) * SAG_SLOT + (j & 3u) * 4u;
-  }
+  // Whether the stage a prologue issue (stage J) or step I of a trip (stage
+  // trip + I + STAGES - 1) sends out starts a group, i.e. carries its load.
+  static constexpr bool sag_issue_prologue(int J) { return SAG && J % 4 == 0; }
+  static constexpr bool sag_issue_step(int I) { return SAG && (I + STAGES - 1) % 4 == 0; }
   __host__ __device__ __forceinline__ static uint32_t sag_lds(uint32_t idx) { return idx * 1024u; }
 
   // Per-task DMA state: buffer descriptors over the task's panels and, for
@@ -559,10 +559,32 @@ struct DmaKernel {
 
   // LDS -> registers, one operand fragment at a time: A fragment I and B
   // fragment J of K step KK of stage buffer S, with their block scales.
-  // sar: whole tasks with A-scale groups, the stage's read offset in the
-  // group ring (sag_read).
+  // The A scales of one stage for the rows of a wave's A fragments, held in
+  // registers (whole tasks with A-scale groups): one dword (4 K blocks) each.
+  struct Scw {
+    uint32_t d[FM];
+  };
+  // A wave reads a group's 16 bytes for each of its fragment rows from the
+  // group slot of stage j: 32 consecutive rows of 16 bytes, conflict-free,
+  // once per group instead of a dword per stage and K step (rows 16 bytes
+  // apart put 32 lanes' dwords on 8 banks).
+  __device__ static __forceinline__ void read_sag(u32x4_t (&sg)[FM], uint32_t j, uint32_t wm) {
+    const uint32_t l32 = threadIdx.x & 31u;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sg[i] = *(const lds_u32x4_t*)(sag_buf<SAG_BYTES>() + sag_slot(j) * SAG_SLOT +
+                                    (wm * TM + i * 32 + l32) * 16u);
+  }
+  __device__ static __forceinline__ Scw scw_of(const u32x4_t (&sg)[FM], int q) {
+    Scw w;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) w.d[i] = sg[i][q];
+    return w;
+  }
+
+  // w: whole tasks with A-scale groups, the stage's A scales (Scw).
   template <int S, int KK, int I, bool FULL>
-  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, uint32_t sar) {
+  __device__ static __forceinline__ void load_a(KFrag& f, uint32_t wm, const Scw& w) {
     const lds_t* base = stage_buf<S, STAGE_BYTES>();
     const lds_t* la = base;
     const lds_t* lsa = base + A_BYTES + B_BYTES;
@@ -579,13 +601,12 @@ struct DmaKernel {
                        (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
     }
     if constexpr (SAG && FULL)
-      f.sa[I] = (*(const lds_u32_t*)(sag_buf<SAG_BYTES>() + sar + row * 16) >> (8 * (2 * KK + hi))) &
-                0xffu;
+      f.sa[I] = (w.d[I] >> (8 * (2 * KK + hi))) & 0xffu;
     else if constexpr (T::SCALED)
       f.sa[I] = (*(const lds_u32_t*)(lsa + row * 4) >> (8 * (2 * KK + hi))) & 0xffu;
     else
       f.sa[I] = 0x7fu;  // 2^0 (the scale operand only matters to fp8 MFMAs)
-    (void)sar;
+    (void)w;
   }
 
   template <int S, int KK, int J>
@@ -640,16 +661,16 @@ struct DmaKernel {
 
   template <int S, int KK, int X, bool FULL>
   __device__ static __forceinline__ void load_one(KFrag& f, uint32_t wm, uint32_t wn,
-                                                 uint32_t sar) {
+                                                 const Scw& w) {
     if constexpr (X < FM)
-      load_a<S, KK, X, FULL>(f, wm, sar);
+      load_a<S, KK, X, FULL>(f, wm, w);
     else
       load_b<S, KK, X - FM>(f, wn);
   }
   template <int S, int KK, bool FULL>
   __device__ static __forceinline__ void load_kstep(KFrag& f, uint32_t wm, uint32_t wn,
-                                                   uint32_t sar) {
-    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value, FULL>(f, wm, wn, sar); });
+                                                   const Scw& w) {
+    static_for<NLK>([&](auto x) { load_one<S, KK, decltype(x)::value, FULL>(f, wm, wn, w); });
   }
 
   // MFMA Q of a K step (A fragment major).
@@ -723,9 +744,12 @@ struct DmaKernel {
   // allowed at the top (-1: no wait and no barrier, the task's last step);
   // LAST: skip the reads that would run past the task's last stage.
   template <int I, bool FULL, bool DMA, int WAITN, bool LAST>
+  // sgc / sgn (whole tasks with A-scale groups): the current and the next
+  // group's A scales of the wave's fragment rows.
   __device__ static __forceinline__ void step_ring(Acc (&acc)[FM][FN], KFrag (&f)[NSET],
                                                    const Ctx& c, const Dma& d, uint32_t kt,
-                                                   uint32_t wm, uint32_t wn, LoopTrace& tr) {
+                                                   uint32_t wm, uint32_t wn, LoopTrace& tr,
+                                                   u32x4_t (&sgc)[FM], u32x4_t (&sgn)[FM]) {
     constexpr int S = I % STAGES, SD = (S + STAGES - 1) % STAGES;
     // Stage kt+1 resident: own DMA done, then the barrier (which also tells
     // that every wave has finished reading stage kt-1, whose buffer the DMA
@@ -737,11 +761,14 @@ struct DmaKernel {
     }
     tr.released();
     const Soff so = stage_so(c, kt + STAGES - 1);
-    // whole tasks with A-scale groups: the stage issued here starts a group
-    // at a fixed step of the trip; the reads of this stage and the next
-    constexpr bool GST = SAG && FULL && (I + STAGES - 1) % 4 == 0;
-    const uint32_t sar0 = (SAG && FULL) ? sag_read(kt) : 0u;
-    const uint32_t sar1 = (SAG && FULL) ? sag_read(kt + 1) : 0u;
+    // whole tasks with A-scale groups: a trip of four steps is one group, so
+    // the stage issued here starts a group at a fixed step (I = 1), and
+    // stage kt is the group's stage I.  The last step reads the next
+    // group's scales (its first stage, kt+1, is resident now).
+    constexpr bool GST = FULL && sag_issue_step(I);
+    if constexpr (SAG && FULL && I == 3 && !LAST) read_sag(sgn, kt + 1, wm);
+    const Scw w0 = (SAG && FULL) ? scw_of(sgc, I % 4) : Scw{};
+    const Scw w1 = (SAG && FULL) ? (I < 3 ? scw_of(sgc, (I + 1) % 4) : scw_of(sgn, 0)) : Scw{};
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
@@ -753,11 +780,15 @@ struct DmaKernel {
         constexpr int SB = (GL / KSTEPS) % STAGES, KL = GL % KSTEPS;
         constexpr bool NEXT = GL / KSTEPS > I;  // the read lies in stage kt+1
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<SB, KL, decltype(x)::value, FULL>(f[GL % NSET], wm, wn, NEXT ? sar1 : sar0);
+          load_one<SB, KL, decltype(x)::value, FULL>(f[GL % NSET], wm, wn, NEXT ? w1 : w0);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    if constexpr (SAG && FULL && I == 3) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sgc[i] = sgn[i];
+    }
   }
 
   template <int I, bool FULL, bool DMA, int WAITN>
@@ -772,9 +803,10 @@ struct DmaKernel {
     tr.released();
     const Soff so = stage_so(c, kt + STAGES - 1);
     constexpr bool GST = SAG && FULL && (I + STAGES - 1) % 4 == 0;
-    const uint32_t sar = (SAG && FULL) ? sag_read(kt) : 0u;
+    static_assert(!SAG, "A-scale groups run with the ring schedule");
+    const Scw w{};
     KFrag g0, g1;
-    load_kstep<S, 0, FULL>(g0, wm, wn, sar);
+    load_kstep<S, 0, FULL>(g0, wm, wn, w);
     static_for<NMF>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KK = Q / NMK, R = Q % NMK;
@@ -782,7 +814,7 @@ struct DmaKernel {
       if constexpr (DMA) slot_dma<SD, Q, FULL, GST>(c, d, so);
       if constexpr (KK + 1 < KSTEPS) {
         static_for_range<(R * NLK) / NMK, ((R + 1) * NLK) / NMK>([&](auto x) {
-          load_one<S, KK + 1, decltype(x)::value, FULL>((KK & 1) ? g0 : g1, wm, wn, sar);
+          load_one<S, KK + 1, decltype(x)::value, FULL>((KK & 1) ? g0 : g1, wm, wn, w);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -795,7 +827,7 @@ struct DmaKernel {
   template <bool FULL>
   __device__ static __forceinline__ void preload_stage0(const Ctx& c) {
     const Dma d = make_dma<FULL>(c);
-    issue<0, FULL, SAG && FULL>(c, d, 0u);
+    issue<0, FULL, FULL && sag_issue_prologue(0)>(c, d, 0u);
   }
 
   // The K loop of one task: nkp (padded, >= UNR) stages from K index c.k0.
@@ -813,17 +845,19 @@ struct DmaKernel {
     uint32_t kt = 0;
     if constexpr (STAGES > 2) {
       // stages 0..STAGES-2 in flight, then stage 0 resident
-      if (!pre) issue<0, FULL, SAG && FULL>(c, d, 0u);
+      if (!pre) issue<0, FULL, FULL && sag_issue_prologue(0)>(c, d, 0u);
       static_for_range<1, STAGES - 1>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        issue<I, FULL, SAG && FULL && I % 4 == 0>(c, d, (uint32_t)I);
+        issue<I, FULL, FULL && sag_issue_prologue(I)>(c, d, (uint32_t)I);
       });
       wait_vm<(STAGES - 2) * LPS>();
       barrier_lds();
+      u32x4_t sgc[FM], sgn[FM];  // A-scale groups: the current and the next group's scales
+      if constexpr (SAG && FULL) read_sag(sgc, 0u, wm);
       KFrag f[NSET];
       static_for<PD>([&](auto g) {
         constexpr int GG = decltype(g)::value;
-        load_kstep<0, GG, FULL>(f[GG], wm, wn, (SAG && FULL) ? sag_read(0u) : 0u);
+        load_kstep<0, GG, FULL>(f[GG], wm, wn, (SAG && FULL) ? scw_of(sgc, 0) : Scw{});
       });
       tr.prologue_done();
       // At the top of step kt the stages up to kt+STAGES-2 have been
@@ -832,7 +866,7 @@ struct DmaKernel {
       for (; kt + UNR < nkp; kt += UNR) {
         static_for<UNR>([&](auto i) {
           constexpr int I = decltype(i)::value;
-          step_ring<I, FULL, true, WSTEADY, false>(acc, f, c, d, kt + I, wm, wn, tr);
+          step_ring<I, FULL, true, WSTEADY, false>(acc, f, c, d, kt + I, wm, wn, tr, sgc, sgn);
         });
       }
       // Last group: only its first step has a stage left to issue (the
@@ -841,7 +875,7 @@ struct DmaKernel {
       static_for<UNR>([&](auto i) {
         constexpr int I = decltype(i)::value;
         constexpr int W = (I == UNR - 1) ? -1 : (I == 0 ? WSTEADY : (STAGES - 2 - I) * LPS);
-        step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr);
+        step_ring<I, FULL, I == 0, W, I == UNR - 1>(acc, f, c, d, kt + I, wm, wn, tr, sgc, sgn);
       });
     } else {
       if (!pre) issue<0, FULL, SAG && FULL>(c, d, 0u);

@@ -280,12 +280,13 @@ void check(const Problem& p) {
 
 // Whole MX tasks with A-scale groups: for the ShuffleK shifts given, walk
 // the task's stages in issue order, check every group load's addresses, and
-// replay the loads and the operand reads on a timeline of loop steps: a load
-// goes out in the step that issues its stage (j - (S - 1); the stages of the
-// prologue before any read), a stage is read in its own step and, with the
-// ring schedule, the step before.  A read must find its group as the slot's
-// last load from an earlier step, and no load may hit a slot in a step that
-// reads it.
+// replay the loads and the reads on a timeline of loop steps: a load goes out
+// in the step that issues its group's first stage (j - (S - 1); the stages
+// of the prologue before any read), and the waves read group g's slot into
+// registers once, in the prologue for group 0 and in step 4g - 1 (the last
+// step of the trip before, with stage 4g resident) for the others.  A read
+// must find its group as the slot's last load from an earlier step, and no
+// load may hit a slot in the step that reads it.
 template <class KN, int BM, int S>
 void check_scale_groups(const Problem& p, const Task& tk, uint32_t k0, uint32_t nk,
                         const GemmArgs& a) {
@@ -298,7 +299,11 @@ void check_scale_groups(const Problem& p, const Task& tk, uint32_t k0, uint32_t 
   for (uint32_t kshift : shifts) {
     std::vector<Load> loads;
     for (uint32_t j = 0; j < nk; ++j) {
-      if (j % 4 != 0) continue;
+      // the kernel's own rule for which issue carries a group load
+      const bool gst = j < (uint32_t)(S - 1) ? KN::sag_issue_prologue((int)j)
+                                            : KN::sag_issue_step((int)((j - (S - 1)) % 4));
+      REQUIRE(gst == (j % 4 == 0), "stage %u group load %d", j, (int)gst);
+      if (!gst) continue;
       const uint32_t kb0 = k0 + ((j + kshift) % nk) * BK;
       const uint32_t slot = KN::sag_slot(j);
       REQUIRE(kb0 / 32 % 16 == 0, "group start stage %u not on a 16-scale boundary", j);
@@ -334,23 +339,25 @@ void check_scale_groups(const Problem& p, const Task& tk, uint32_t k0, uint32_t 
       const int64_t t = j < (uint32_t)(S - 1) ? -2 : (int64_t)j - (S - 1);
       loads.push_back(Load{t, slot, (int64_t)(kb0 / 32 / 16)});
     }
-    for (uint32_t j = 0; j < nk; ++j) {
-      const uint32_t kidx = (j + kshift) % nk, kb0 = k0 + kidx * BK;
-      const uint32_t slot = KN::sag_slot(j), sar = KN::sag_read(j);
-      REQUIRE(sar == slot * KN::SAG_SLOT + (kidx % 4) * 4, "stage %u reads offset %u", j, sar);
-      for (int64_t tr = (S >= 3 ? (int64_t)j - 1 : (int64_t)j); tr <= (int64_t)j; ++tr) {
-        const Load* last = nullptr;
-        for (const Load& l : loads) {
-          if (l.slot != slot) continue;
-          REQUIRE(l.t != tr, "slot %u loaded in step %lld, which reads stage %u", slot,
-                  (long long)tr, j);
-          if (l.t < tr && (!last || l.t > last->t)) last = &l;
-        }
-        ++g_checked;
-        REQUIRE(last && last->group == (int64_t)(kb0 / 32 / 16),
-                "%s stage %u (step %lld) finds group %lld in slot %u, wants %u", p.name.c_str(), j,
-                (long long)tr, last ? (long long)last->group : -1LL, slot, kb0 / 32 / 16);
+    for (uint32_t g = 0; g < nk / 4; ++g) {
+      const uint32_t kb0 = k0 + ((4 * g + kshift) % nk) * BK;
+      const uint32_t slot = KN::sag_slot(4 * g);
+      const int64_t tr = g == 0 ? -1 : 4 * (int64_t)g - 1;
+      // every stage of the group reads its scales from these registers: the
+      // group's four stages are its 16 bytes in order
+      for (uint32_t q = 0; q < 4; ++q)
+        REQUIRE(k0 + ((4 * g + q + kshift) % nk) * BK == kb0 + q * BK && KN::sag_slot(4 * g + q) == slot,
+                "group %u stage %u out of order", g, q);
+      const Load* last = nullptr;
+      for (const Load& l : loads) {
+        if (l.slot != slot) continue;
+        REQUIRE(l.t != tr, "slot %u loaded in step %lld, which reads it", slot, (long long)tr);
+        if (l.t < tr && (!last || l.t > last->t)) last = &l;
       }
+      ++g_checked;
+      REQUIRE(last && last->group == (int64_t)(kb0 / 32 / 16),
+              "%s group %u (step %lld) finds group %lld in slot %u, wants %u", p.name.c_str(), g,
+              (long long)tr, last ? (long long)last->group : -1LL, slot, kb0 / 32 / 16);
     }
   }
 }
