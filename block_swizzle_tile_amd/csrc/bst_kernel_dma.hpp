@@ -683,10 +683,12 @@ struct DmaKernel {
   // The DMA instructions that MFMA slot Q of a stage carries.  A wave
   // blocks while it issues a DMA instruction and its MFMA pipe drains
   // meanwhile, so each one sits right behind an MFMA instead of in a burst.
-  // With 3 or more stages the LPS instructions are dealt out evenly over the
-  // NMF slots; with 2 the stage in flight has only the current stage's
-  // compute to land in, so its instructions go one per slot from the first.
-  static constexpr int DSLOTS = (STAGES == 2 && LPS < NMF) ? LPS : NMF;
+  // With 4 or more stages the LPS instructions are dealt out evenly over the
+  // NMF slots: the stage issued in step kt must be resident two steps later.
+  // With 2 or 3 stages it has only one step's compute to land in (with 3,
+  // the ring reads stage kt+2 from the top of step kt+1 on), so its
+  // instructions go one per slot from the first.
+  static constexpr int DSLOTS = (STAGES <= 3 && LPS < NMF) ? LPS : NMF;
   template <int SD, int Q, bool FULL, bool GST>
   __device__ static __forceinline__ void slot_dma(const Ctx& c, const Dma& d, const Soff& so) {
     if constexpr (Q < DSLOTS)
